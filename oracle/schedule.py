@@ -1,0 +1,165 @@
+"""Oracle for the context-parallel schedules: zigzag sharding, the ring's
+per-step block kinds, and emulations of the ring (P2P), Ulysses (A2A) and USP
+shares built only from ``oracle.attention``.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg; never by the library.
+
+Sources:
+
+* nougat.kr, "MaxText long-context training: KV parallelism", diagram text
+  (sequence split; All-gather; A2A; P2P) and section "헤드를 나누거나, KV를
+  돌리거나" (split the heads, or rotate the KV): the sequence is split by
+  tokens; a ring rank keeps its own KV chunk and one visiting chunk, computes
+  a partial result, merges it and receives the next chunk; later tokens see
+  more context, so the causal work must be balanced across ranks; A2A turns
+  the token split into a head split; USP combines an A2A group with a ring.
+* siliconandsystems.com, "Llama 3 parallelism", section "긴 문맥은 어텐션 비용
+  이상을 바꾸는 방식" (long context changes more than the attention cost): work
+  is to be balanced by actual attention compute.
+
+The balancing scheme itself is not spelled out on the pages.  The reading used
+here ("zigzag"): cut the S tokens into 2P equal chunks; rank r holds chunks r
+and 2P-1-r; ring step s brings rank (r - s) mod P's KV.  S must be a multiple
+of 2P.  Arrays in "sharded order" concatenate the ranks' local shards:
+rank 0's two chunks, then rank 1's, and so on.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import attention as A
+
+SKIP, DIAG, FULL = 0, 1, 2
+
+
+def zigzag_layout(S, P, r):
+    """Global start and length of rank r's two chunks: ((r*c, (2P-1-r)*c), (c, c))."""
+    if P < 1 or S % (2 * P) != 0 or not 0 <= r < P:
+        raise ValueError("need P >= 1, S divisible by 2P and 0 <= r < P")
+    c = S // (2 * P)
+    return (r * c, (2 * P - 1 - r) * c), (c, c)
+
+
+def rank_positions(S, P, r):
+    """Global positions of rank r's local tokens, in local order."""
+    (p0, p1), (l0, l1) = zigzag_layout(S, P, r)
+    return np.concatenate([np.arange(p0, p0 + l0), np.arange(p1, p1 + l1)])
+
+
+def sharded_order(S, P):
+    """Global position of each row of a sharded-order array."""
+    return np.concatenate([rank_positions(S, P, r) for r in range(P)])
+
+
+def ring_source(P, r, s):
+    """Rank whose KV chunk rank r holds at ring step s (neighbour passing)."""
+    return (r - s) % P
+
+
+def ring_schedule(S, P, r, s):
+    """(source rank, kinds[4]) for rank r at step s.
+
+    kinds[a*2 + b] classifies local Q chunk a of rank r against local KV chunk
+    b of the source rank at chunk granularity under the causal mask: SKIP if
+    the KV chunk lies after the Q chunk, DIAG if it is the same chunk, FULL if
+    it lies before.
+    """
+    zigzag_layout(S, P, r)
+    src = ring_source(P, r, s)
+    qchunks = (r, 2 * P - 1 - r)
+    kchunks = (src, 2 * P - 1 - src)
+    kinds = []
+    for a in range(2):
+        for b in range(2):
+            if kchunks[b] > qchunks[a]:
+                kinds.append(SKIP)
+            elif kchunks[b] == qchunks[a]:
+                kinds.append(DIAG)
+            else:
+                kinds.append(FULL)
+    return src, kinds
+
+
+def causal_pairs(qpos, kpos):
+    """Number of (query, key) pairs with key position <= query position."""
+    return int(A.allowed_mask(qpos, kpos, True).sum())
+
+
+def _shard(x, S, P, r):
+    c2 = S // P
+    return x[r * c2:(r + 1) * c2]
+
+
+def ring_forward(q, k, v, S, P, r, *, scale, causal=True, doc=None):
+    """Rank r's forward under the ring, all inputs in sharded order.
+
+    At each step the rank's Q shard attends to the visiting KV shard (every
+    mask entry evaluated on global positions), and the partial (O, LSE) is
+    merged into the running result.  Returns (o, lse, steps) where steps is the
+    list of per-step partials (o_s, lse_s).
+    """
+    qpos = rank_positions(S, P, r)
+    qd = None if doc is None else _shard(doc, S, P, r)
+    qs = _shard(q, S, P, r)
+    o = lse = None
+    steps = []
+    for s in range(P):
+        j = ring_source(P, r, s)
+        kpos = rank_positions(S, P, j)
+        kd = None if doc is None else _shard(doc, S, P, j)
+        po, pl = A.forward(qs, _shard(k, S, P, j), _shard(v, S, P, j), qpos, kpos,
+                           scale=scale, causal=causal, qdoc=qd, kdoc=kd)
+        steps.append((po, pl))
+        if o is None:
+            o, lse = po, pl
+        else:
+            o, lse = A.merge(o, lse, po, pl)
+    return o, lse, steps
+
+
+def ring_backward(q, k, v, dout, o, lse, S, P, r, *, scale, causal=True, doc=None):
+    """Rank r's backward under the ring (sharded order).
+
+    Delta comes from the rank's final O; each step's chunk backward uses the
+    final LSE.  Returns (dq of the rank's rows, dk, dv over all S rows) where
+    dk/dv hold only this rank's query rows' contributions, each in the
+    visiting rank's slot: what a ring carries back to each KV owner.
+    """
+    qpos = rank_positions(S, P, r)
+    qd = None if doc is None else _shard(doc, S, P, r)
+    qs = _shard(q, S, P, r)
+    dlt = A.delta(o, dout)
+    dq = np.zeros(qs.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    c2 = S // P
+    for s in range(P):
+        j = ring_source(P, r, s)
+        kd = None if doc is None else _shard(doc, S, P, j)
+        gq, gk, gv = A.backward(qs, _shard(k, S, P, j), _shard(v, S, P, j), dout,
+                                lse, dlt, qpos, rank_positions(S, P, j),
+                                scale=scale, causal=causal, qdoc=qd, kdoc=kd)
+        dq += gq
+        dk[j * c2:(j + 1) * c2] += gk
+        dv[j * c2:(j + 1) * c2] += gv
+    return dq, dk, dv
+
+
+def head_slice(hq, hkv, sp, rank):
+    """Query and KV head ranges of Ulysses rank ``rank`` out of ``sp``: the
+    all-to-all hands each rank a contiguous slice of heads for the whole
+    sequence (nougat.kr MaxText page, A2A diagram text)."""
+    if hq % sp or hkv % sp:
+        raise ValueError("sp must divide both the query and the KV head counts")
+    a, b = hq // sp, hkv // sp
+    return (rank * a, (rank + 1) * a), (rank * b, (rank + 1) * b)
+
+
+def ulysses_share(q, k, v, sp, rank, *, scale, causal=True, doc=None):
+    """Ulysses rank's share: full-sequence attention for its head slice.
+    q [S, Hq, d], k/v [S, Hkv, d] in global order (the layer's full heads)."""
+    (h0, h1), (g0, g1) = head_slice(q.shape[1], k.shape[1], sp, rank)
+    pos = np.arange(q.shape[0])
+    return A.forward(q[:, h0:h1], k[:, g0:g1], v[:, g0:g1], pos, pos,
+                     scale=scale, causal=causal, qdoc=doc, kdoc=doc)
