@@ -1,0 +1,297 @@
+"""Benchmark of one GPU's share of context-parallel attention on MI355X.
+
+Default workload: the Ulysses share of a Llama-3.1-8B-shaped layer at SP=4:
+the full S=65536 causal sequence for this GPU's 8 query heads / 2 KV heads,
+d=128, bf16, forward + backward (dO ~ N(0,1)).  One step = one
+cp_ulysses_share call with the backward (zero-fill of the gradients, forward
+chunk attention, Delta, backward chunk attention), all in libcpattn's kernels.
+
+Prints ONE JSON line.  ``value`` is the causal-FLOP throughput of the step:
+algorithmic FLOPs (4*d per allowed (query, key) pair per query head forward,
+10*d backward) divided by the step time.  ``roofline`` describes the dominant
+kernel (timed alone with HIP events on its stream), ``cpu_baseline`` the
+fp64 oracle timed on the host cores on a bounded sample.
+
+Other workloads (``--workload``): ring_128k (rank 0 of a zigzag ring of
+P=8 over S=131072, 32/8 heads), docs_128k (S=131072 packed lognormal
+documents, 32/8 heads), usp_1m (rank 0 of a 4-rank ring over S=1,048,576 for
+an 8/2 head slice).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
+METRIC = "causal attn fwd+bwd TFLOPS & tokens/s, 64K GQA32/8 d128 bf16; % MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="ulysses_64k",
+                    choices=["ulysses_64k", "ring_128k", "docs_128k", "usp_1m"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    return ap.parse_args()
+
+
+def causal_pairs_zigzag_rank(S, P):
+    c = S // (2 * P)
+    return P * 2 * c * c + c
+
+
+class Workload:
+    """Seeded synthetic inputs of one configuration, resident in HBM."""
+
+    def __init__(self, name, torch, cp, cpinputs):
+        self.name = name
+        dev = "cuda"
+        bf = torch.bfloat16
+        self.dev = dev
+        if name == "ulysses_64k":
+            S, hq, hkv, d, sp = 65536, 32, 8, 128, 4
+            self.S, self.hq, self.hkv, self.d = S, hq // sp, hkv // sp, d
+            seed = cpinputs.SEEDS["ulysses_64k"]
+            # the share after the all-to-all: 8 query heads, 2 KV heads, full sequence
+            self.q, self.k, self.v, self.dout = cpinputs.normal_torch(
+                seed, [(S, self.hq, d), (S, self.hkv, d), (S, self.hkv, d), (S, self.hq, d)], dev, bf)
+            self.doc = None
+            self.rows = S
+            self.pairs_per_head = S * (S + 1) // 2
+            self.tokens = S
+            self.group = sp
+            self.config = {"workload": "ulysses_share_sp4", "S": S, "heads_q": self.hq, "heads_kv": self.hkv,
+                           "layer_heads": f"{hq}/{hkv}", "d": d, "causal": True, "sp": sp}
+        elif name in ("ring_128k", "usp_1m"):
+            if name == "ring_128k":
+                S, hq, hkv, d, P = 131072, 32, 8, 128, 8
+            else:
+                S, hq, hkv, d, P = 1048576, 8, 2, 128, 4
+            self.S, self.hq, self.hkv, self.d, self.P = S, hq, hkv, d, P
+            seed = cpinputs.SEEDS[name]
+            n = S // P
+            # every rank's shard, in sharded order (random data: order is immaterial)
+            self.q, self.k, self.v = cpinputs.normal_torch(seed, [(n, hq, d), (S, hkv, d), (S, hkv, d)], dev, bf)
+            (self.dout,) = cpinputs.normal_torch(seed + 1, [(n, hq, d)], dev, bf)
+            self.doc = None
+            self.rows = n
+            self.pairs_per_head = causal_pairs_zigzag_rank(S, P)
+            self.tokens = S
+            self.group = P if name == "ring_128k" else 16
+            self.config = {"workload": "ring_rank0_zigzag" if name == "ring_128k" else "usp_share_a2a4_ring4",
+                           "S": S, "P": P, "local_q": n, "heads_q": hq, "heads_kv": hkv, "d": d, "causal": True}
+        else:
+            S, hq, hkv, d = 131072, 32, 8, 128
+            self.S, self.hq, self.hkv, self.d = S, hq, hkv, d
+            seed = cpinputs.SEEDS["docs_128k"]
+            self.q, self.k, self.v, self.dout = cpinputs.normal_torch(
+                seed, [(S, hq, d), (S, hkv, d), (S, hkv, d), (S, hq, d)], dev, bf)
+            lens = cpinputs.lognormal_doc_lengths(S)
+            self.doc = torch.from_numpy(cpinputs.doc_ids_from_lengths(lens)).to(dev)
+            self.rows = S
+            self.pairs_per_head = int(sum(int(L) * (int(L) + 1) // 2 for L in lens))
+            self.tokens = S
+            self.group = 1
+            self.config = {"workload": "packed_docs", "S": S, "heads_q": hq, "heads_kv": hkv, "d": d,
+                           "causal": True, "docs": int(len(lens)), "doc_len_median": 4096, "doc_sigma": 1.0}
+        self.flops_fwd = 4 * self.d * self.pairs_per_head * self.hq
+        self.flops_bwd = 10 * self.d * self.pairs_per_head * self.hq
+        hq, hkv, d, rows = self.hq, self.hkv, self.d, self.rows
+        self.o = torch.empty(rows, hq, d, device=dev, dtype=bf)
+        self.lse_shape = (hq, rows)
+        self.lse = torch.empty(hq, rows, device=dev)
+        self.dq = torch.empty(rows, hq, d, device=dev)
+        kv_rows = self.k.shape[0]
+        self.dk = torch.empty(kv_rows, hkv, d, device=dev)
+        self.dv = torch.empty_like(self.dk)
+        self.delta = torch.empty(hq, rows, device=dev)
+        self.sh = cp.make_shape(hq, hkv, d, hq * d, hkv * d, 1.0 / math.sqrt(d), True, cp.CP_BF16)
+        if name in ("ring_128k", "usp_1m"):
+            self.ws = cp.workspace(cp.cp_ring_workspace_bytes(self.sh, self.S, self.P, 0, cp.CP_BF16, True))
+        else:
+            self.ws = cp.workspace(cp.cp_ulysses_workspace_bytes(self.sh, self.S, 1, True))
+
+    def step(self, cp):
+        if self.name in ("ring_128k", "usp_1m"):
+            # this GPU is rank 0; the KV for the steps is every rank's shard
+            cp.cp_ring_emulate(self.sh, self.S, self.P, 0, self.q_full_rank0(), self.k, self.v, None,
+                               self.o, self.lse, self.dout, self.dq, self.dk, self.dv, workspace=self.ws)
+        else:
+            cp.cp_ulysses_share(self.sh, self.S, 1, 0, self.q, self.k, self.v, self.doc, self.o, self.lse,
+                                self.dout, self.dq, self.dk, self.dv, workspace=self.ws)
+
+    def q_full_rank0(self):
+        # cp_ring_emulate reads rank r's Q rows at offset r * S/P of a sharded
+        # array; rank 0's rows are first, so the rank-0 shard alone suffices.
+        return self.q
+
+
+def kernel_times(wl, cp, torch, iters):
+    """Average duration (ms) of the forward and backward chunk kernels alone,
+    HIP events on the stream they are launched on."""
+    st = torch.cuda.current_stream()
+    if wl.name in ("ring_128k", "usp_1m"):
+        S, P = wl.S, wl.P
+        c = S // (2 * P)
+        n = S // P
+        qs = cp.make_span(0, c, (2 * P - 1) * c, c)
+        ks = cp.make_span(0, c, (2 * P - 1) * c, c)           # step 0: the rank's own KV
+        k, v = wl.k[:n], wl.v[:n]
+        pairs = 2 * c * c + c
+        dk = wl.dk[:n]
+        dv = wl.dv[:n]
+    else:
+        qs = cp.make_span(0, wl.rows, 0, 0, wl.doc)
+        ks = cp.make_span(0, wl.rows, 0, 0, wl.doc)
+        k, v = wl.k, wl.v
+        pairs = wl.pairs_per_head
+        dk, dv = wl.dk, wl.dv
+    o32 = torch.empty(wl.rows, wl.hq, wl.d, device=wl.dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    cp.cp_attn_chunk_fwd(wl.sh, wl.q, qs, k, v, ks, wl.o, wl.lse)
+    cp.cp_attn_delta(wl.o, wl.dout, wl.delta)
+    torch.cuda.synchronize()
+    ev[0].record(st)
+    for _ in range(iters):
+        cp.cp_attn_chunk_fwd(wl.sh, wl.q, qs, k, v, ks, o32, wl.lse)
+    ev[1].record(st)
+    for _ in range(iters):
+        cp.cp_attn_chunk_bwd(wl.sh, wl.q, qs, k, v, ks, wl.dout, wl.lse, wl.delta, wl.dq, dk, dv)
+    ev[2].record(st)
+    torch.cuda.synchronize()
+    t_fwd = ev[0].elapsed_time(ev[1]) / iters
+    t_bwd = ev[1].elapsed_time(ev[2]) / iters
+    return t_fwd, t_bwd, 4 * wl.d * pairs * wl.hq, 10 * wl.d * pairs * wl.hq
+
+
+def sampled_parity(wl, torch):
+    """Max error of O, LSE and dQ on 16 sampled rows of one query head vs the
+    fp64 oracle (every sampled row exact over all its keys)."""
+    from oracle import attention as A
+    if wl.name != "ulysses_64k":
+        return None
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(wl.S, size=16, replace=False))
+    heads = rng.integers(0, wl.hq, size=16)
+    q = wl.q.float().cpu().numpy()
+    k = wl.k.float().cpu().numpy()
+    v = wl.v.float().cpu().numpy()
+    do = wl.dout.float().cpu().numpy()
+    pos = np.arange(wl.S)
+    scale = 1.0 / math.sqrt(wl.d)
+    o, lse = A.forward_rows(q, k, v, pos, pos, rows, heads, scale=scale, causal=True)
+    dlt = np.einsum("ne,ne->n", o, do[rows, heads].astype(np.float64))
+    dq = A.dq_rows(q, k, v, do, lse, dlt, pos, pos, rows, heads, scale=scale, causal=True)
+    go = wl.o.float().cpu().numpy()[rows, heads]
+    gl = wl.lse.cpu().numpy()[heads, rows]
+    gdq = wl.dq.cpu().numpy()[rows, heads]
+    return {"rows": 16, "o": float(np.abs(go - o).max()), "lse": float(np.abs(gl - lse).max()),
+            "dq": float(np.abs(gdq - dq).max())}
+
+
+def cpu_baseline(wl):
+    """The oracle (untuned) on the host cores: forward + backward of one KV
+    group (hq/hkv query heads sharing one KV head) over the first 8192 tokens
+    of the causal sequence, in causal-FLOP TFLOPS."""
+    import torch
+    from oracle import attention as A
+    L = 8192
+    g = wl.hq // wl.hkv
+    q = wl.q[:L, :g].float().cpu().numpy()
+    k = wl.k[:L, :1].float().cpu().numpy()
+    v = wl.v[:L, :1].float().cpu().numpy()
+    do = wl.dout[:L, :g].float().cpu().numpy()
+    pos = np.arange(L)
+    scale = 1.0 / math.sqrt(wl.d)
+    t0 = time.perf_counter()
+    o, lse = A.forward(q, k, v, pos, pos, scale=scale, causal=True)
+    A.backward(q, k, v, do, lse, A.delta(o, do), pos, pos, scale=scale, causal=True)
+    t = time.perf_counter() - t0
+    flops = 14 * wl.d * (L * (L + 1) // 2) * g
+    cores = len(os.sched_getaffinity(0))
+    return {"value": flops / t / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 numpy oracle, forward+backward of one KV group ({g} query heads) over the "
+                      f"first {L} tokens, causal; {t:.1f} s",
+            "seconds": t, "torch_threads": torch.get_num_threads()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported "
+              "(this build runs on a single GPU, with no collectives)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import cpinputs
+    import sequence_context_parallelism_amd as cp
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    cp.load()
+    wl = Workload(args.workload, torch, cp, cpinputs)
+    torch.cuda.synchronize()
+    print(f"[bench] workload {args.workload} ready", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        wl.step(cp)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(args.steps):
+        wl.step(cp)
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    parity = sampled_parity(wl, torch)
+
+    flops = wl.flops_fwd + wl.flops_bwd
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": wl.config,
+        "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1),
+        "tokens_per_s_per_gpu": round(wl.tokens / (ms * 1e-3) / wl.group, 1),
+        "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "flops_per_step": flops, "wall_s_timed": round(wall, 3),
+        "max_memory_allocated_gib": round(torch.cuda.max_memory_allocated() / 2**30, 2),
+    }
+    if parity:
+        out["parity_sample"] = parity
+    if not args.no_kernel_timing:
+        t_fwd, t_bwd, f_fwd, f_bwd = kernel_times(wl, cp, torch, max(3, args.steps))
+        fw = f_fwd / (t_fwd * 1e-3) / 1e12
+        bw = f_bwd / (t_bwd * 1e-3) / 1e12
+        dom = ("bwd_bf16_kernel", bw, t_bwd) if t_bwd >= t_fwd else ("fwd_bf16_kernel", fw, t_fwd)
+        out["kernels"] = {"fwd_ms": round(t_fwd, 4), "fwd_tflops": round(fw, 1),
+                          "bwd_ms": round(t_bwd, 4), "bwd_tflops": round(bw, 1)}
+        out["roofline"] = {"kernel": dom[0], "bound": "mfma", "achieved": round(dom[1], 1),
+                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(dom[1] / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -35,8 +35,8 @@ SKIP, DIAG, FULL = 0, 1, 2
 
 def zigzag_layout(S, P, r):
     """Global start and length of rank r's two chunks: ((r*c, (2P-1-r)*c), (c, c))."""
-    if P < 1 or S % (2 * P) != 0 or not 0 <= r < P:
-        raise ValueError("need P >= 1, S divisible by 2P and 0 <= r < P")
+    if P < 1 or S < 1 or S % (2 * P) != 0 or not 0 <= r < P:
+        raise ValueError("need P >= 1, S > 0 divisible by 2P and 0 <= r < P")
     c = S // (2 * P)
     return (r * c, (2 * P - 1 - r) * c), (c, c)
 

@@ -1,0 +1,214 @@
+"""Python binding of libcpattn: one GPU's share of context-parallel attention
+on MI355X.
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels of
+``libcpattn.so``; PyTorch supplies device memory and the stream.  Each
+function has the name of the C entry point it wraps (see include/cpattn.h for
+layouts, ownership and error behaviour) and raises ``CpError`` on any status
+other than CP_OK.  There is no fallback: if the library is missing, ``load``
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcpattn.so")
+
+CP_OK, CP_ERR_ARG, CP_ERR_UNSUPPORTED, CP_ERR_ALIGN, CP_ERR_DOCS, CP_ERR_WORKSPACE, CP_ERR_HIP = \
+    0, -1, -2, -3, -4, -5, -6
+CP_BF16, CP_F32 = 0, 1
+
+EXPORTED = (
+    "cp_attn_chunk_fwd", "cp_lse_merge", "cp_attn_delta", "cp_attn_chunk_bwd",
+    "cp_zigzag_layout", "cp_ring_schedule", "cp_ring_workspace_bytes", "cp_ring_emulate",
+    "cp_ulysses_workspace_bytes", "cp_ulysses_share", "cp_tile_map", "cp_last_error",
+    "cp_abi_version",
+)
+
+
+class CpError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"cpattn status {status}: {message}")
+        self.status = status
+
+
+class cp_span(ctypes.Structure):
+    _fields_ = [("pos", ctypes.c_int64 * 2), ("len", ctypes.c_int32 * 2),
+                ("doc", ctypes.c_void_p)]
+
+
+class cp_shape(ctypes.Structure):
+    _fields_ = [("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("q_stride", ctypes.c_int64), ("kv_stride", ctypes.c_int64),
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libcpattn.so (once).  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m sequence_context_parallelism_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    SH = ctypes.POINTER(cp_shape)
+    sig = {
+        "cp_attn_chunk_fwd": (I32, [SH, P, cp_span, P, P, cp_span, P, I32, P, P]),
+        "cp_lse_merge": (I32, [I64, I32, I32, P, P, P, P, P]),
+        "cp_attn_delta": (I32, [I64, I32, I32, P, I32, P, I32, P, P]),
+        "cp_attn_chunk_bwd": (I32, [SH, P, cp_span, P, P, cp_span, P, P, P, P, P, P, P]),
+        "cp_zigzag_layout": (I32, [I64, I32, I32, ctypes.POINTER(ctypes.c_int64),
+                                   ctypes.POINTER(ctypes.c_int32)]),
+        "cp_ring_schedule": (I32, [I64, I32, I32, I32, ctypes.POINTER(ctypes.c_int32),
+                                   ctypes.POINTER(ctypes.c_int8)]),
+        "cp_ring_workspace_bytes": (SZ, [SH, I64, I32, I32, I32, I32]),
+        "cp_ring_emulate": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, P, P,
+                                  P, SZ, P]),
+        "cp_ulysses_workspace_bytes": (SZ, [SH, I64, I32, I32]),
+        "cp_ulysses_share": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, P,
+                                   SZ, P]),
+        "cp_tile_map": (I32, [SH, cp_span, cp_span, I32, I32, P, P]),
+        "cp_last_error": (ctypes.c_char_p, []),
+        "cp_abi_version": (I32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != CP_OK:
+        raise CpError(status, _lib.cp_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return CP_BF16
+    if t.dtype == torch.float32:
+        return CP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def make_span(pos0, len0, pos1=0, len1=0, doc=None):
+    """A cp_span of up to two runs of global positions; ``doc`` is an int32
+    device tensor or None."""
+    s = cp_span()
+    s.pos[0], s.pos[1] = int(pos0), int(pos1)
+    s.len[0], s.len[1] = int(len0), int(len1)
+    s.doc = None if doc is None else doc.data_ptr()
+    return s
+
+
+def make_shape(hq, hkv, d, q_stride, kv_stride, scale, causal, dtype):
+    sh = cp_shape()
+    sh.hq, sh.hkv, sh.d = hq, hkv, d
+    sh.q_stride, sh.kv_stride = q_stride, kv_stride
+    sh.scale, sh.causal, sh.dtype = scale, int(bool(causal)), dtype
+    return sh
+
+
+def cp_abi_version():
+    return load().cp_abi_version()
+
+
+def cp_attn_chunk_fwd(shape, q, qs, k, v, ks, o, lse, stream=None):
+    lib = load()
+    _check(lib.cp_attn_chunk_fwd(ctypes.byref(shape), _ptr(q), qs, _ptr(k), _ptr(v), ks,
+                                 _ptr(o), _dtype_code(o), _ptr(lse), _stream(stream)))
+
+
+def cp_lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
+    """o_* [rows, h, d] fp32, lse_* [h, rows] fp32; acc updated in place."""
+    lib = load()
+    rows, h, d = o_acc.shape
+    _check(lib.cp_lse_merge(rows, h, d, _ptr(o_acc), _ptr(lse_acc), _ptr(o_part),
+                            _ptr(lse_part), _stream(stream)))
+
+
+def cp_attn_delta(o, dout, delta, stream=None):
+    lib = load()
+    rows, h, d = o.shape
+    _check(lib.cp_attn_delta(rows, h, d, _ptr(o), _dtype_code(o), _ptr(dout), _dtype_code(dout),
+                             _ptr(delta), _stream(stream)))
+
+
+def cp_attn_chunk_bwd(shape, q, qs, k, v, ks, dout, lse, delta, dq, dk, dv, stream=None):
+    lib = load()
+    _check(lib.cp_attn_chunk_bwd(ctypes.byref(shape), _ptr(q), qs, _ptr(k), _ptr(v), ks,
+                                 _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _stream(stream)))
+
+
+def cp_zigzag_layout(S, P, rank):
+    lib = load()
+    pos = (ctypes.c_int64 * 2)()
+    ln = (ctypes.c_int32 * 2)()
+    _check(lib.cp_zigzag_layout(S, P, rank, pos, ln))
+    return (pos[0], pos[1]), (ln[0], ln[1])
+
+
+def cp_ring_schedule(S, P, rank, step):
+    lib = load()
+    src = ctypes.c_int32()
+    kind = (ctypes.c_int8 * 4)()
+    _check(lib.cp_ring_schedule(S, P, rank, step, ctypes.byref(src), kind))
+    return src.value, [kind[i] for i in range(4)]
+
+
+def cp_ring_workspace_bytes(shape, S, P, rank, o_dtype, backward):
+    return load().cp_ring_workspace_bytes(ctypes.byref(shape), S, P, rank, o_dtype, int(bool(backward)))
+
+
+def cp_ring_emulate(shape, S, P, rank, q, k, v, doc, o, lse, dout=None, dq=None, dk=None, dv=None,
+                    step_o=None, step_lse=None, workspace=None, stream=None):
+    lib = load()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.cp_ring_emulate(ctypes.byref(shape), S, P, rank, _ptr(q), _ptr(k), _ptr(v), _ptr(doc),
+                               _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                               _ptr(dv), _ptr(step_o), _ptr(step_lse), _ptr(workspace), ws_bytes,
+                               _stream(stream)))
+
+
+def cp_ulysses_workspace_bytes(shape, S, sp, backward):
+    return load().cp_ulysses_workspace_bytes(ctypes.byref(shape), S, sp, int(bool(backward)))
+
+
+def cp_ulysses_share(shape, S, sp, sp_rank, q, k, v, doc, o, lse, dout=None, dq=None, dk=None,
+                     dv=None, workspace=None, stream=None):
+    lib = load()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.cp_ulysses_share(ctypes.byref(shape), S, sp, sp_rank, _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(doc), _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def cp_tile_map(shape, qs, ks, bq, bk, out, stream=None):
+    lib = load()
+    _check(lib.cp_tile_map(ctypes.byref(shape), qs, ks, bq, bk, _ptr(out), _stream(stream)))
+
+
+def workspace(nbytes, device="cuda"):
+    """A caller-owned scratch buffer (torch allocations are 256-byte aligned)."""
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)

@@ -1,0 +1,438 @@
+// Host side of libcpattn: argument validation, the C-ABI entry points declared
+// in include/cpattn.h, and the ring / Ulysses drivers that sequence the
+// kernels on the caller's stream.  No allocation happens here: every buffer,
+// including scratch, belongs to the caller.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/cpattn.h"
+#include "kernels.h"
+
+using namespace cp;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cp_status fail(cp_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+cp_status ok() {
+  g_last_error.clear();
+  return CP_OK;
+}
+
+cp_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elt_size(cp_dtype t) { return t == CP_F32 ? 4 : 2; }
+
+bool valid_dtype(cp_dtype t) { return t == CP_BF16 || t == CP_F32; }
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+cp_status check_shape(const cp_shape* sh) {
+  if (!sh) return fail(CP_ERR_ARG, "shape is NULL");
+  if (sh->hq <= 0 || sh->hkv <= 0) return fail(CP_ERR_ARG, "hq=%d and hkv=%d must be positive", sh->hq, sh->hkv);
+  if (sh->hq % sh->hkv != 0) return fail(CP_ERR_ARG, "hq=%d is not a multiple of hkv=%d", sh->hq, sh->hkv);
+  const int g = sh->hq / sh->hkv;
+  if ((g & (g - 1)) != 0 || g > 64)
+    return fail(CP_ERR_UNSUPPORTED, "group size hq/hkv=%d must be a power of two <= 64", g);
+  if (sh->d != 64 && sh->d != 128) return fail(CP_ERR_UNSUPPORTED, "head dim d=%d not in {64, 128}", sh->d);
+  if (!valid_dtype(sh->dtype)) return fail(CP_ERR_ARG, "unknown dtype %d", (int)sh->dtype);
+  if (!(sh->scale > 0.f) || sh->scale != sh->scale) return fail(CP_ERR_ARG, "scale must be positive and finite");
+  if (sh->causal != 0 && sh->causal != 1) return fail(CP_ERR_ARG, "causal must be 0 or 1");
+  const size_t esz = elt_size(sh->dtype);
+  if (sh->q_stride < (int64_t)sh->hq * sh->d) return fail(CP_ERR_ARG, "q_stride %lld < hq*d", (long long)sh->q_stride);
+  if (sh->kv_stride < (int64_t)sh->hkv * sh->d) return fail(CP_ERR_ARG, "kv_stride %lld < hkv*d", (long long)sh->kv_stride);
+  if ((sh->q_stride * esz) % 16 || (sh->kv_stride * esz) % 16)
+    return fail(CP_ERR_ALIGN, "token strides must be multiples of 16 bytes");
+  return CP_OK;
+}
+
+cp_status check_span(const cp_span& s, const char* name) {
+  if (s.len[0] < 0 || s.len[1] < 0) return fail(CP_ERR_ARG, "%s: negative length", name);
+  if ((int64_t)s.len[0] + s.len[1] > INT32_MAX) return fail(CP_ERR_ARG, "%s: too long", name);
+  if (s.len[1] > 0 && s.pos[1] < s.pos[0] + s.len[0])
+    return fail(CP_ERR_ARG, "%s: second run must start at or after the end of the first", name);
+  return CP_OK;
+}
+
+SpanD to_dev(const cp_span& s) { return SpanD{s.pos[0], s.pos[1], s.len[0], s.len[1], s.doc}; }
+
+int32_t span_total(const cp_span& s) { return s.len[0] + s.len[1]; }
+
+cp_span run_span(int64_t p0, int32_t l0, int64_t p1, int32_t l1, const int32_t* doc) {
+  cp_span s;
+  s.pos[0] = p0; s.pos[1] = p1; s.len[0] = l0; s.len[1] = l1; s.doc = doc;
+  return s;
+}
+
+// ---- unchecked launchers shared by the entry points and the drivers ----
+hipError_t run_fwd(const cp_shape* sh, const void* q, const cp_span& qs, const void* k, const void* v,
+                   const cp_span& ks, void* o, cp_dtype o_dtype, float* lse, int64_t lse_ld,
+                   hipStream_t st) {
+  FwdParams p{};
+  p.q = (const __bf16*)q; p.k = (const __bf16*)k; p.v = (const __bf16*)v;
+  p.qf = (const float*)q; p.kf = (const float*)k; p.vf = (const float*)v;
+  p.q_stride = sh->q_stride; p.kv_stride = sh->kv_stride;
+  p.qs = to_dev(qs); p.ks = to_dev(ks);
+  p.hq = sh->hq; p.hkv = sh->hkv; p.G = sh->hq / sh->hkv; p.d = sh->d;
+  p.scale = sh->scale; p.causal = sh->causal;
+  p.o = o; p.o_f32 = o_dtype == CP_F32; p.lse = lse; p.lse_ld = lse_ld;
+  return sh->dtype == CP_F32 ? launch_fwd_f32(p, st) : launch_fwd_bf16(p, st);
+}
+
+hipError_t run_bwd(const cp_shape* sh, const void* q, const cp_span& qs, const void* k, const void* v,
+                   const cp_span& ks, const void* dout, const float* lse, const float* delta,
+                   int64_t lse_ld, float* dq, float* dk, float* dv, hipStream_t st) {
+  BwdParams p{};
+  p.q = (const __bf16*)q; p.k = (const __bf16*)k; p.v = (const __bf16*)v; p.dout = (const __bf16*)dout;
+  p.qf = (const float*)q; p.kf = (const float*)k; p.vf = (const float*)v; p.doutf = (const float*)dout;
+  p.q_stride = sh->q_stride; p.kv_stride = sh->kv_stride;
+  p.qs = to_dev(qs); p.ks = to_dev(ks);
+  p.hq = sh->hq; p.hkv = sh->hkv; p.G = sh->hq / sh->hkv; p.d = sh->d;
+  p.scale = sh->scale; p.causal = sh->causal;
+  p.lse = lse; p.delta = delta; p.lse_ld = lse_ld;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  return sh->dtype == CP_F32 ? launch_bwd_f32(p, st) : launch_bwd_bf16(p, st);
+}
+
+#define CP_TRY_HIP(expr, what)                 \
+  do {                                         \
+    hipError_t e_ = (expr);                    \
+    if (e_ != hipSuccess) return hip_status(e_, what); \
+  } while (0)
+
+#define CP_TRY(expr)                           \
+  do {                                         \
+    cp_status s_ = (expr);                     \
+    if (s_ != CP_OK) return s_;                \
+  } while (0)
+
+cp_status check_docs(const cp_span& a, const cp_span& b) {
+  if ((a.doc == nullptr) != (b.doc == nullptr))
+    return fail(CP_ERR_DOCS, "doc ids must be given for both the query and the key span, or neither");
+  return CP_OK;
+}
+
+cp_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(CP_ERR_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(CP_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return CP_OK;
+}
+
+struct RingLayout {
+  size_t acc_o, part_o, part_lse, delta, total;
+};
+
+RingLayout ring_layout(const cp_shape* sh, int64_t n, cp_dtype o_dtype, bool backward) {
+  RingLayout L{};
+  const size_t obytes = align256((size_t)n * sh->hq * sh->d * 4);
+  const size_t lbytes = align256((size_t)n * sh->hq * 4);
+  size_t off = 0;
+  L.acc_o = off; if (o_dtype == CP_BF16) off += obytes;
+  L.part_o = off; off += obytes;
+  L.part_lse = off; off += lbytes;
+  L.delta = off; if (backward) off += lbytes;
+  L.total = off;
+  return L;
+}
+
+cp_status check_ring_args(const cp_shape* sh, int64_t S, int32_t P, int32_t rank) {
+  CP_TRY(check_shape(sh));
+  if (P < 1) return fail(CP_ERR_ARG, "P=%d must be >= 1", P);
+  if (S <= 0 || S % (2 * (int64_t)P) != 0) return fail(CP_ERR_ARG, "S=%lld must be a positive multiple of 2P=%d", (long long)S, 2 * P);
+  if (S > INT32_MAX) return fail(CP_ERR_ARG, "S=%lld too large", (long long)S);
+  if (rank < -1 || rank >= P) return fail(CP_ERR_ARG, "rank=%d out of [-1, P)", rank);
+  return CP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t cp_abi_version(void) { return CP_ABI_VERSION; }
+
+const char* cp_last_error(void) { return g_last_error.c_str(); }
+
+cp_status cp_attn_chunk_fwd(const cp_shape* sh, const void* q, cp_span qs, const void* k, const void* v,
+                            cp_span ks, void* o, cp_dtype o_dtype, float* lse, void* stream) {
+  CP_TRY(check_shape(sh));
+  CP_TRY(check_span(qs, "qs"));
+  CP_TRY(check_span(ks, "ks"));
+  CP_TRY(check_docs(qs, ks));
+  if (!valid_dtype(o_dtype)) return fail(CP_ERR_ARG, "unknown o_dtype");
+  const int32_t Lq = span_total(qs), Lk = span_total(ks);
+  if (Lq == 0) return ok();
+  CP_TRY(check_ptr(q, "q"));
+  CP_TRY(check_ptr(o, "o"));
+  CP_TRY(check_ptr(lse, "lse"));
+  if (Lk > 0) { CP_TRY(check_ptr(k, "k")); CP_TRY(check_ptr(v, "v")); }
+  CP_TRY_HIP(run_fwd(sh, q, qs, k, v, ks, o, o_dtype, lse, Lq, (hipStream_t)stream), "cp_attn_chunk_fwd");
+  return ok();
+}
+
+cp_status cp_lse_merge(int64_t rows, int32_t h, int32_t d, float* o_acc, float* lse_acc, const float* o_part,
+                       const float* lse_part, void* stream) {
+  if (rows < 0 || h <= 0) return fail(CP_ERR_ARG, "rows=%lld, h=%d", (long long)rows, h);
+  if (d != 64 && d != 128) return fail(CP_ERR_UNSUPPORTED, "d=%d not in {64, 128}", d);
+  if (rows == 0) return ok();
+  CP_TRY(check_ptr(o_acc, "o_acc"));
+  CP_TRY(check_ptr(o_part, "o_part"));
+  if (!lse_acc || !lse_part) return fail(CP_ERR_ARG, "lse pointer is NULL");
+  CP_TRY_HIP(launch_lse_merge(rows, h, d, o_acc, lse_acc, rows, o_part, lse_part, rows, (hipStream_t)stream),
+             "cp_lse_merge");
+  return ok();
+}
+
+cp_status cp_attn_delta(int64_t rows, int32_t h, int32_t d, const void* o, cp_dtype o_dtype, const void* dout,
+                        cp_dtype dout_dtype, float* delta, void* stream) {
+  if (rows < 0 || h <= 0) return fail(CP_ERR_ARG, "rows=%lld, h=%d", (long long)rows, h);
+  if (d != 64 && d != 128) return fail(CP_ERR_UNSUPPORTED, "d=%d not in {64, 128}", d);
+  if (!valid_dtype(o_dtype) || !valid_dtype(dout_dtype)) return fail(CP_ERR_ARG, "unknown dtype");
+  if (rows == 0) return ok();
+  CP_TRY(check_ptr(o, "o"));
+  CP_TRY(check_ptr(dout, "dout"));
+  if (!delta) return fail(CP_ERR_ARG, "delta is NULL");
+  CP_TRY_HIP(launch_delta(rows, h, d, o, o_dtype == CP_F32, dout, dout_dtype == CP_F32, delta, rows,
+                          (hipStream_t)stream), "cp_attn_delta");
+  return ok();
+}
+
+cp_status cp_attn_chunk_bwd(const cp_shape* sh, const void* q, cp_span qs, const void* k, const void* v,
+                            cp_span ks, const void* dout, const float* lse, const float* delta, float* dq,
+                            float* dk, float* dv, void* stream) {
+  CP_TRY(check_shape(sh));
+  CP_TRY(check_span(qs, "qs"));
+  CP_TRY(check_span(ks, "ks"));
+  CP_TRY(check_docs(qs, ks));
+  const int32_t Lq = span_total(qs), Lk = span_total(ks);
+  if (Lq == 0 || Lk == 0) return ok();
+  CP_TRY(check_ptr(q, "q"));
+  CP_TRY(check_ptr(k, "k"));
+  CP_TRY(check_ptr(v, "v"));
+  CP_TRY(check_ptr(dout, "dout"));
+  CP_TRY(check_ptr(dq, "dq"));
+  CP_TRY(check_ptr(dk, "dk"));
+  CP_TRY(check_ptr(dv, "dv"));
+  if (!lse || !delta) return fail(CP_ERR_ARG, "lse or delta is NULL");
+  CP_TRY_HIP(run_bwd(sh, q, qs, k, v, ks, dout, lse, delta, Lq, dq, dk, dv, (hipStream_t)stream),
+             "cp_attn_chunk_bwd");
+  return ok();
+}
+
+cp_status cp_zigzag_layout(int64_t S, int32_t P, int32_t rank, int64_t pos0[2], int32_t len[2]) {
+  if (!pos0 || !len) return fail(CP_ERR_ARG, "output pointer is NULL");
+  if (P < 1 || S <= 0 || S % (2 * (int64_t)P) != 0 || rank < 0 || rank >= P)
+    return fail(CP_ERR_ARG, "need P >= 1, S > 0 divisible by 2P and 0 <= rank < P (S=%lld P=%d rank=%d)",
+                (long long)S, P, rank);
+  const int64_t c = S / (2 * P);
+  if (c > INT32_MAX) return fail(CP_ERR_ARG, "chunk too long");
+  pos0[0] = rank * c;
+  pos0[1] = (2 * (int64_t)P - 1 - rank) * c;
+  len[0] = (int32_t)c;
+  len[1] = (int32_t)c;
+  return ok();
+}
+
+cp_status cp_ring_schedule(int64_t S, int32_t P, int32_t rank, int32_t step, int32_t* src_rank, int8_t kind[4]) {
+  if (!src_rank || !kind) return fail(CP_ERR_ARG, "output pointer is NULL");
+  int64_t pos0[2];
+  int32_t len[2];
+  CP_TRY(cp_zigzag_layout(S, P, rank, pos0, len));
+  if (step < 0 || step >= P) return fail(CP_ERR_ARG, "step=%d out of [0, P)", step);
+  const int32_t src = ((rank - step) % P + P) % P;
+  const int32_t qc[2] = {rank, 2 * P - 1 - rank};
+  const int32_t kc[2] = {src, 2 * P - 1 - src};
+  for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 2; ++b) kind[a * 2 + b] = kc[b] > qc[a] ? 0 : (kc[b] == qc[a] ? 1 : 2);
+  *src_rank = src;
+  return ok();
+}
+
+size_t cp_ring_workspace_bytes(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, cp_dtype o_dtype,
+                               int32_t backward) {
+  if (check_ring_args(sh, S, P, rank) != CP_OK || !valid_dtype(o_dtype)) return 0;
+  return ring_layout(sh, S / P, o_dtype, backward != 0).total;
+}
+
+cp_status cp_ring_emulate(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, const void* q, const void* k,
+                          const void* v, const int32_t* doc, void* o, cp_dtype o_dtype, float* lse,
+                          const void* dout, float* dq, float* dk, float* dv, float* step_o, float* step_lse,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  CP_TRY(check_ring_args(sh, S, P, rank));
+  if (!valid_dtype(o_dtype)) return fail(CP_ERR_ARG, "unknown o_dtype");
+  CP_TRY(check_ptr(q, "q"));
+  CP_TRY(check_ptr(k, "k"));
+  CP_TRY(check_ptr(v, "v"));
+  CP_TRY(check_ptr(o, "o"));
+  if (!lse) return fail(CP_ERR_ARG, "lse is NULL");
+  const bool backward = dout != nullptr;
+  if (backward) {
+    CP_TRY(check_ptr(dout, "dout"));
+    CP_TRY(check_ptr(dq, "dq"));
+    CP_TRY(check_ptr(dk, "dk"));
+    CP_TRY(check_ptr(dv, "dv"));
+  }
+  if ((step_o == nullptr) != (step_lse == nullptr))
+    return fail(CP_ERR_ARG, "step_o and step_lse must both be given or both be NULL");
+  if (step_o && rank < 0) return fail(CP_ERR_ARG, "per-step capture needs a single rank");
+  if (step_o) CP_TRY(check_ptr(step_o, "step_o"));
+  const int64_t n = S / P;                       // rows per rank = 2c
+  const int32_t c = (int32_t)(S / (2 * P));
+  const RingLayout lay = ring_layout(sh, n, o_dtype, backward);
+  if (lay.total > 0) {
+    if (!workspace) return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes required", lay.total);
+    if (ws_bytes < lay.total) return fail(CP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, lay.total);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(CP_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* acc_o_ws = (float*)(ws + lay.acc_o);
+  float* part_o = (float*)(ws + lay.part_o);
+  float* part_lse = (float*)(ws + lay.part_lse);
+  float* dlt = (float*)(ws + lay.delta);
+
+  const size_t in_esz = elt_size(sh->dtype), o_esz = elt_size(o_dtype);
+  const int64_t orow = (int64_t)sh->hq * sh->d;          // elements per output row
+  const int64_t kvrow = (int64_t)sh->hkv * sh->d;
+
+  if (backward) {
+    const int64_t dq_rows = rank < 0 ? S : n;
+    CP_TRY_HIP(launch_fill_zero(dq_rows * orow, dq, st), "zero dq");
+    CP_TRY_HIP(launch_fill_zero(S * kvrow, dk, st), "zero dk");
+    CP_TRY_HIP(launch_fill_zero(S * kvrow, dv, st), "zero dv");
+  }
+
+  const int32_t r0 = rank < 0 ? 0 : rank, r1 = rank < 0 ? P : rank + 1;
+  for (int32_t r = r0; r < r1; ++r) {
+    const int64_t out_row0 = rank < 0 ? (int64_t)r * n : 0;       // row offset into o / dq
+    const char* qr = (const char*)q + (size_t)r * n * sh->q_stride * in_esz;
+    const cp_span qs = run_span((int64_t)r * c, c, (int64_t)(2 * P - 1 - r) * c, c, doc ? doc + r * n : nullptr);
+    char* o_r = (char*)o + (size_t)out_row0 * orow * o_esz;
+    float* lse_r = lse + (rank < 0 ? (size_t)r * sh->hq * n : 0);
+    float* acc_o = o_dtype == CP_F32 ? (float*)o_r : acc_o_ws;
+
+    for (int32_t s = 0; s < P; ++s) {
+      const int32_t j = ((r - s) % P + P) % P;
+      const char* kj = (const char*)k + (size_t)j * n * sh->kv_stride * in_esz;
+      const char* vj = (const char*)v + (size_t)j * n * sh->kv_stride * in_esz;
+      const cp_span ks = run_span((int64_t)j * c, c, (int64_t)(2 * P - 1 - j) * c, c, doc ? doc + j * n : nullptr);
+      float* so = step_o ? step_o + (size_t)s * n * orow : (s == 0 ? acc_o : part_o);
+      float* sl = step_lse ? step_lse + (size_t)s * sh->hq * n : (s == 0 ? lse_r : part_lse);
+      CP_TRY_HIP(run_fwd(sh, qr, qs, kj, vj, ks, so, CP_F32, sl, n, st), "ring forward step");
+      if (s == 0) {
+        if (step_o) {
+          CP_TRY_HIP(launch_copy_f32(n * orow, so, acc_o, st), "ring copy");
+          CP_TRY_HIP(launch_copy_f32(n * sh->hq, sl, lse_r, st), "ring copy");
+        }
+      } else {
+        CP_TRY_HIP(launch_lse_merge(n, sh->hq, sh->d, acc_o, lse_r, n, so, sl, n, st), "ring merge");
+      }
+    }
+    if (o_dtype == CP_BF16) CP_TRY_HIP(launch_f32_to_bf16(n * orow, acc_o, (__bf16*)o_r, st), "ring convert");
+
+    if (backward) {
+      const char* dout_r = (const char*)dout + (size_t)out_row0 * orow * in_esz;
+      float* dq_r = dq + (size_t)out_row0 * orow;
+      CP_TRY_HIP(launch_delta(n, sh->hq, sh->d, o_r, o_dtype == CP_F32, dout_r, sh->dtype == CP_F32, dlt, n, st),
+                 "ring delta");
+      for (int32_t s = 0; s < P; ++s) {
+        const int32_t j = ((r - s) % P + P) % P;
+        const char* kj = (const char*)k + (size_t)j * n * sh->kv_stride * in_esz;
+        const char* vj = (const char*)v + (size_t)j * n * sh->kv_stride * in_esz;
+        const cp_span ks = run_span((int64_t)j * c, c, (int64_t)(2 * P - 1 - j) * c, c, doc ? doc + j * n : nullptr);
+        CP_TRY_HIP(run_bwd(sh, qr, qs, kj, vj, ks, dout_r, lse_r, dlt, n, dq_r, dk + (size_t)j * n * kvrow,
+                           dv + (size_t)j * n * kvrow, st), "ring backward step");
+      }
+    }
+  }
+  return ok();
+}
+
+size_t cp_ulysses_workspace_bytes(const cp_shape* sh, int64_t S, int32_t sp, int32_t backward) {
+  if (check_shape(sh) != CP_OK || S <= 0 || sp < 1 || sh->hq % sp || sh->hkv % sp) return 0;
+  return backward ? align256((size_t)(sh->hq / sp) * S * 4) : 0;
+}
+
+cp_status cp_ulysses_share(const cp_shape* sh_full, int64_t S, int32_t sp, int32_t sp_rank, const void* q,
+                           const void* k, const void* v, const int32_t* doc, void* o, cp_dtype o_dtype, float* lse,
+                           const void* dout, float* dq, float* dk, float* dv, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  CP_TRY(check_shape(sh_full));
+  if (S <= 0 || S > INT32_MAX) return fail(CP_ERR_ARG, "S=%lld out of range", (long long)S);
+  if (sp < 1 || sp_rank < 0 || sp_rank >= sp) return fail(CP_ERR_ARG, "sp=%d, sp_rank=%d", sp, sp_rank);
+  if (sh_full->hq % sp || sh_full->hkv % sp)
+    return fail(CP_ERR_ARG, "sp=%d must divide hq=%d and hkv=%d (KV heads bound the Ulysses degree)", sp,
+                sh_full->hq, sh_full->hkv);
+  if (!valid_dtype(o_dtype)) return fail(CP_ERR_ARG, "unknown o_dtype");
+  CP_TRY(check_ptr(q, "q"));
+  CP_TRY(check_ptr(k, "k"));
+  CP_TRY(check_ptr(v, "v"));
+  CP_TRY(check_ptr(o, "o"));
+  if (!lse) return fail(CP_ERR_ARG, "lse is NULL");
+  const bool backward = dout != nullptr;
+  if (backward) {
+    CP_TRY(check_ptr(dout, "dout"));
+    CP_TRY(check_ptr(dq, "dq"));
+    CP_TRY(check_ptr(dk, "dk"));
+    CP_TRY(check_ptr(dv, "dv"));
+    const size_t need = cp_ulysses_workspace_bytes(sh_full, S, sp, 1);
+    if (!workspace || ws_bytes < need) return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(CP_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  cp_shape sh = *sh_full;
+  sh.hq = sh_full->hq / sp;
+  sh.hkv = sh_full->hkv / sp;
+  const size_t esz = elt_size(sh.dtype);
+  const char* qs_ptr = (const char*)q + (size_t)sp_rank * sh.hq * sh.d * esz;
+  const char* ks_ptr = (const char*)k + (size_t)sp_rank * sh.hkv * sh.d * esz;
+  const char* vs_ptr = (const char*)v + (size_t)sp_rank * sh.hkv * sh.d * esz;
+  if (!aligned16(qs_ptr) || !aligned16(ks_ptr)) return fail(CP_ERR_ALIGN, "head slice not 16-byte aligned");
+  const cp_span span = run_span(0, (int32_t)S, S, 0, doc);
+  hipStream_t st = (hipStream_t)stream;
+  CP_TRY_HIP(run_fwd(&sh, qs_ptr, span, ks_ptr, vs_ptr, span, o, o_dtype, lse, S, st), "ulysses forward");
+  if (backward) {
+    float* dlt = (float*)workspace;
+    const int64_t orow = (int64_t)sh.hq * sh.d, kvrow = (int64_t)sh.hkv * sh.d;
+    CP_TRY_HIP(launch_fill_zero(S * orow, dq, st), "zero dq");
+    CP_TRY_HIP(launch_fill_zero(S * kvrow, dk, st), "zero dk");
+    CP_TRY_HIP(launch_fill_zero(S * kvrow, dv, st), "zero dv");
+    CP_TRY_HIP(launch_delta(S, sh.hq, sh.d, o, o_dtype == CP_F32, dout, sh.dtype == CP_F32, dlt, S, st),
+               "ulysses delta");
+    CP_TRY_HIP(run_bwd(&sh, qs_ptr, span, ks_ptr, vs_ptr, span, dout, lse, dlt, S, dq, dk, dv, st),
+               "ulysses backward");
+  }
+  return ok();
+}
+
+cp_status cp_tile_map(const cp_shape* sh, cp_span qs, cp_span ks, int32_t bq, int32_t bk, int8_t* out,
+                      void* stream) {
+  CP_TRY(check_shape(sh));
+  CP_TRY(check_span(qs, "qs"));
+  CP_TRY(check_span(ks, "ks"));
+  CP_TRY(check_docs(qs, ks));
+  if (bq <= 0 || bk <= 0) return fail(CP_ERR_ARG, "tile sizes must be positive");
+  if (span_total(qs) == 0 || span_total(ks) == 0) return ok();
+  if (!out) return fail(CP_ERR_ARG, "out is NULL");
+  CP_TRY_HIP(launch_tile_map(to_dev(qs), to_dev(ks), sh->causal, bq, bk, out, (hipStream_t)stream),
+             "cp_tile_map");
+  return ok();
+}
+
+}  // extern "C"

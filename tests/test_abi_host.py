@@ -1,0 +1,118 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol the header
+declares, and its host-only logic (zigzag layout, ring schedule, argument
+validation) matches the oracle bit for bit.  No kernel is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sequence_context_parallelism_amd as cp
+from oracle import schedule as Z
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cp_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return cp.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 13
+    assert set(names) == set(cp.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert cp.cp_abi_version() == 1
+
+
+@pytest.mark.parametrize("S,P", [(16, 2), (256, 2), (131072, 8), (1048576, 4), (96, 6), (8, 1)])
+def test_zigzag_and_schedule_bit_exact(S, P):
+    for r in range(P):
+        assert cp.cp_zigzag_layout(S, P, r) == tuple(tuple(x) for x in Z.zigzag_layout(S, P, r))
+        for s in range(P):
+            src, kinds = cp.cp_ring_schedule(S, P, r, s)
+            osrc, okinds = Z.ring_schedule(S, P, r, s)
+            assert (src, kinds) == (osrc, okinds)
+
+
+@pytest.mark.parametrize("args", [(10, 3, 0), (16, 2, 2), (16, 0, 0), (16, 2, -1), (0, 1, 0)])
+def test_zigzag_rejects_bad_sizes(args):
+    with pytest.raises(cp.CpError) as e:
+        cp.cp_zigzag_layout(*args)
+    assert e.value.status == cp.CP_ERR_ARG
+    with pytest.raises(ValueError):
+        Z.zigzag_layout(*args)
+
+
+def test_schedule_rejects_bad_step():
+    with pytest.raises(cp.CpError):
+        cp.cp_ring_schedule(16, 2, 0, 2)
+
+
+def _shape(**kw):
+    base = dict(hq=8, hkv=2, d=128, q_stride=8 * 128, kv_stride=2 * 128, scale=0.088,
+                causal=True, dtype=cp.CP_BF16)
+    base.update(kw)
+    return cp.make_shape(**base)
+
+
+def _fwd_status(lib, shape, qs=None, ks=None, ptr=0x10000):
+    qs = qs or cp.make_span(0, 64)
+    ks = ks or cp.make_span(0, 64)
+    p = ctypes.c_void_p(ptr)
+    return lib.cp_attn_chunk_fwd(ctypes.byref(shape), p, qs, p, p, ks, p, cp.CP_F32, p, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), cp.CP_ERR_UNSUPPORTED),
+    (dict(hq=6, hkv=2), cp.CP_ERR_UNSUPPORTED),       # group of 3
+    (dict(hq=7, hkv=2), cp.CP_ERR_ARG),
+    (dict(q_stride=100), cp.CP_ERR_ARG),
+    (dict(q_stride=8 * 128 + 4), cp.CP_ERR_ALIGN),
+    (dict(scale=-1.0), cp.CP_ERR_ARG),
+    (dict(hkv=0), cp.CP_ERR_ARG),
+])
+def test_validation_errors_before_launch(lib, kw, status):
+    assert _fwd_status(lib, _shape(**kw)) == status
+    assert lib.cp_last_error().decode() != ""
+
+
+def test_span_and_pointer_errors(lib):
+    sh = _shape()
+    bad_runs = cp.make_span(0, 64, 10, 8)                  # second run overlaps the first
+    assert _fwd_status(lib, sh, qs=bad_runs) == cp.CP_ERR_ARG
+    assert _fwd_status(lib, sh, qs=cp.make_span(0, -1)) == cp.CP_ERR_ARG
+    assert _fwd_status(lib, sh, ptr=0x10008) == cp.CP_ERR_ALIGN
+    one_doc = cp.cp_span()
+    one_doc.len[0] = 64
+    one_doc.doc = 0x1000
+    assert _fwd_status(lib, sh, qs=one_doc) == cp.CP_ERR_DOCS
+    # empty query span: nothing to do, success without touching memory
+    assert _fwd_status(lib, sh, qs=cp.make_span(0, 0)) == cp.CP_OK
+
+
+def test_ring_and_ulysses_argument_errors(lib):
+    sh = _shape()
+    P = ctypes.c_void_p(0x10000)
+    st = lib.cp_ring_emulate(ctypes.byref(sh), 1000, 8, 0, P, P, P, None, P, cp.CP_BF16, P,
+                             None, None, None, None, None, None, None, 0, None)
+    assert st == cp.CP_ERR_ARG                                  # 1000 % 16 != 0
+    st = lib.cp_ring_emulate(ctypes.byref(sh), 1024, 8, 0, P, P, P, None, P, cp.CP_BF16, P,
+                             None, None, None, None, None, None, None, 0, None)
+    assert st == cp.CP_ERR_WORKSPACE
+    need = cp.cp_ring_workspace_bytes(sh, 1024, 8, 0, cp.CP_BF16, False)
+    assert need > 0 and need % 256 == 0
+    st = lib.cp_ulysses_share(ctypes.byref(sh), 1024, 4, 0, P, P, P, None, P, cp.CP_BF16, P,
+                              None, None, None, None, None, 0, None)
+    assert st == cp.CP_ERR_ARG                                  # sp=4 does not divide hkv=2
+    assert cp.cp_ulysses_workspace_bytes(sh, 1024, 2, True) == 4 * 1024 * 4
