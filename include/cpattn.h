@@ -131,9 +131,8 @@ cp_status cp_attn_delta(int64_t rows, int32_t h, int32_t d, const void *o, cp_dt
 /* Backward of one chunk pair from the saved FINAL lse and delta (P is
  * recomputed).  Accumulates (+=) into dq [Lq, hq, d], dk and dv [Lk, hkv, d],
  * all fp32: callers zero them first.  dout: [Lq, hq, d] in sh->dtype.
- * dk/dv are summed over the query heads of each KV group.  The bf16 path adds
- * dq with fp32 atomics (summation order, hence the last bits, may vary from
- * run to run); dk and dv are deterministic. */
+ * dk/dv are summed over the query heads of each KV group.  No atomics are
+ * used: repeated calls on the same inputs give bitwise-identical results. */
 cp_status cp_attn_chunk_bwd(const cp_shape *sh, const void *q, cp_span qs,
                             const void *k, const void *v, cp_span ks, const void *dout,
                             const float *lse, const float *delta,

@@ -1,99 +1,130 @@
 // Backward chunk attention, bf16 inputs, fp32 accumulation, CDNA4 (gfx950).
 //
-// Given the final (merged) row LSE and Delta = rowsum(dO * O), accumulates
-// this chunk pair's contribution to dQ, dK and dV: the gradient of the masked
+// Given the final (merged) row LSE and Delta = rowsum(dO * O), adds this
+// chunk pair's contribution to dQ, dK and dV: the gradient of the masked
 // softmax attention whose forward is in attn_fwd_bf16.hip.  The pages do not
 // describe the backward; it is the derivative of that definition, with P
 // recomputed from the saved LSE (the recompute-in-backward idea behind
 // activation checkpointing, siliconandsystems.com "Llama 3 parallelism",
 // section on long context changing more than the attention cost).
 //
-// Work decomposition (KV-outer)
-//   * one work-group = 4 waves = 128 keys of one KV head; wave w owns 32 keys,
-//     whose K and V rows it keeps in VGPRs as MFMA B operands and whose dK^T
-//     and dV^T accumulators it keeps for the whole kernel.
-//   * the group streams query tiles of 64 rows for every query head of the
-//     GQA group; each tile of Q and dO is staged in LDS twice: row-major (the
-//     A operand when contracting over d) and interleaved by 4 rows (the A
-//     operand when contracting over queries).  The next tile's global loads
-//     are issued before the current tile's MFMAs.
-//   * per tile and wave: S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_bf16,
-//     accumulator lane = key, 16 query rows), P = exp2(S*c - LSE2),
-//     dS = scale * P * (dP - Delta); dV^T += dO^T P and dK^T += Q^T dS take P
-//     and dS straight from the accumulator layout as B operands.
-//   * dQ = dS K needs all 128 keys: dS goes through LDS and each wave computes
-//     32 of the d columns, then adds them to the fp32 dQ with global atomics.
-//   * fully masked tiles are skipped; element masks only on partial or ragged
-//     tiles.  Heavy-first order: earlier keys are seen by more queries.
+// Two kernels, neither with atomics (deterministic):
+//   dkdv (KV-outer): a work-group owns 128 keys of one KV head (32 per wave,
+//     their K and V rows held in VGPRs as MFMA B operands and their dK^T,
+//     dV^T accumulators in AGPRs) and streams 64-row tiles of Q and dO for
+//     every query head of the GQA group through LDS (direct-to-LDS loads,
+//     double-buffered).  Per tile: S = Q K^T, dP = dO V^T (A operands read
+//     row-wise), P = exp2(S c - LSE log2 e), dS = scale P (dP - Delta), then
+//     dV^T += dO^T P and dK^T += Q^T dS (A operands read with the LDS
+//     transpose read; P and dS go from the accumulator layout straight into
+//     the B operand).  4 MFMA products per (query, key) pair.
+//   dq (Q-outer): a work-group owns 64 query rows of 4 query heads sharing a
+//     KV head (like the forward) and streams 64-key tiles of K and V.  Per
+//     tile: S^T = K Q^T, dP^T = V dO^T, P^T, dS^T, dQ^T += K^T dS^T.  3 MFMA
+//     products per pair (S and dP are recomputed rather than exchanged).
+// Fully masked tiles are skipped; element masks only on partial or ragged
+// tiles.  Heavy-first orders: ascending keys for dkdv, descending queries for
+// dq.
 #include "common.h"
 #include "kernels.h"
+#include "tile_io.h"
 
 namespace cp {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
-constexpr int BQ = 64;    // query rows per tile
-constexpr int BKW = 32;   // keys per wave
-constexpr int BKG = 128;  // keys per work-group
+constexpr int BQ = 64;     // query rows per tile (dkdv) / per wave (dq)
+constexpr int BKW = 32;    // keys per wave (dkdv)
+constexpr int BKG = 128;   // keys per work-group (dkdv)
+constexpr int BK = 64;     // keys per tile (dq)
 constexpr float LOG2E = 1.4426950408889634f;
 
+__device__ inline void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ============================== dK, dV ======================================
+
 template <int D>
-struct Lds {
-  static constexpr int RST = D + 8;                  // padded row-major stride
-  static constexpr int QR = 0;                        // Q row-major  [64][RST]
-  static constexpr int DOR = QR + BQ * RST * 2;       // dO row-major [64][RST]
-  static constexpr int QI = DOR + BQ * RST * 2;       // Q  [16][D][4]
-  static constexpr int DOI = QI + BQ * D * 2;         // dO [16][D][4]
-  static constexpr int DS = DOI + BQ * D * 2;         // dS [64][BKG + 8]
-  static constexpr int DSST = BKG + 8;
-  static constexpr int KI = DS + BQ * DSST * 2;       // K  [32][D][4]
-  static constexpr int LSE = KI + BKG * D * 2;        // lse2 [64]
-  static constexpr int DLT = LSE + BQ * 4;            // delta [64]
-  static constexpr int QDOC = DLT + BQ * 4;           // query doc ids [64]
-  static constexpr int TOTAL = QDOC + BQ * 4;
+struct KvState {
+  bf16x8 kf[D / 16], vf[D / 16];   // this wave's 32 keys as B operands
+  f32x16 dka[D / 32], dva[D / 32]; // dK^T, dV^T accumulators [d block]
+  int32_t qlim;                    // queries [qlim, ..) see this lane's key causally
+  int32_t kdoc;
+  bool kvalid;
 };
 
-// interleave 4 rows x 8 dims (4 x 16-byte pieces) into 8 pieces of 4 rows
-__device__ inline void store_interleaved(__bf16* dst, int D, int rg, int dg, const u32x4 r[4]) {
+// one (64-query tile, head) step for one wave
+template <int D>
+__device__ inline void dkdv_tile(KvState<D>& st, const char* Qt, const char* Ot, const float* Lt,
+                                 const float* Dlt, const int32_t* QDt, int32_t qa0, int32_t Lq, bool mask,
+                                 bool docs, float c, float scale, int lane) {
+  const int lq = lane & 31, hh = lane >> 5;
+  const int s16 = lane & 15, cg = (lane >> 4) & 1;
+  f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    u32x2 lo, hi;
-    lo.x = __builtin_amdgcn_perm(r[1][m], r[0][m], 0x05040100u);
-    lo.y = __builtin_amdgcn_perm(r[3][m], r[2][m], 0x05040100u);
-    hi.x = __builtin_amdgcn_perm(r[1][m], r[0][m], 0x07060302u);
-    hi.y = __builtin_amdgcn_perm(r[3][m], r[2][m], 0x07060302u);
-    int d0 = dg * 8 + 2 * m;
-    *(u32x2*)(dst + ((rg * D) + d0) * 4) = lo;
-    *(u32x2*)(dst + ((rg * D) + d0 + 1) * 4) = hi;
+  for (int kd = 0; kd < D / 16; ++kd) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const bf16x8 qa = lds_row8<D>(Qt, qb * 32 + lq, kd * 16 + hh * 8);
+      const bf16x8 oa = lds_row8<D>(Ot, qb * 32 + lq, kd * 16 + hh * 8);
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, st.kf[kd], s[qb], 0, 0, 0);
+      dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, st.vf[kd], dp[qb], 0, 0, 0);
+    }
+  }
+  // accumulator element r of block qb: key = lane's key, query row qb*32 + 8(r/4) + 4hh + r%4
+  bf16x8 pf[4], dsf[4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int qr0 = qb * 32 + j * 8 + hh * 4;
+      const f32x4 l4 = *(const f32x4*)(Lt + qr0);
+      const f32x4 d4 = *(const f32x4*)(Dlt + qr0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = j * 4 + i;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -l4[i] * LOG2E));
+        if (mask) {
+          const int32_t qidx = qa0 + qr0 + i;
+          const bool ok = st.kvalid & (qidx < Lq) & (qidx >= st.qlim) & (!docs | (QDt[qr0 + i] == st.kdoc));
+          p = ok ? p : 0.f;
+        }
+        const float ds = p * (dp[qb][r] - d4[i]) * scale;
+        const int t = qb * 2 + (r >> 3), sl = r & 7;
+        pf[t][sl] = (__bf16)p;
+        dsf[t][sl] = (__bf16)ds;
+      }
+    }
+  }
+  // dV^T += dO^T P, dK^T += Q^T dS: A operands = transposed reads of the tiles
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c0 = db * 32 + 16 * cg;
+      const bf16x8 oa = cat8(lds_tr4<D>(Ot, 16 * t + 4 * hh, c0, s16), lds_tr4<D>(Ot, 16 * t + 8 + 4 * hh, c0, s16));
+      const bf16x8 qa = cat8(lds_tr4<D>(Qt, 16 * t + 4 * hh, c0, s16), lds_tr4<D>(Qt, 16 * t + 8 + 4 * hh, c0, s16));
+      st.dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pf[t], st.dva[db], 0, 0, 0);
+      st.dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsf[t], st.dka[db], 0, 0, 0);
+    }
   }
 }
 
-__device__ inline bf16x8 read_interleaved(const __bf16* src, int D, int t, int hh, int d) {
-  u32x2 lo = *(const u32x2*)(src + ((4 * t + hh) * D + d) * 4);
-  u32x2 hi = *(const u32x2*)(src + ((4 * t + 2 + hh) * D + d) * 4);
-  u32x4 v = {lo.x, lo.y, hi.x, hi.y};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams a) {
-  using L = Lds<D>;
-  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-  __bf16* Qr = (__bf16*)(smem + L::QR);
-  __bf16* dOr = (__bf16*)(smem + L::DOR);
-  __bf16* Qi = (__bf16*)(smem + L::QI);
-  __bf16* dOi = (__bf16*)(smem + L::DOI);
-  __bf16* dSl = (__bf16*)(smem + L::DS);
-  __bf16* Ki = (__bf16*)(smem + L::KI);
-  float* lse2 = (float*)(smem + L::LSE);
-  float* dlt = (float*)(smem + L::DLT);
-  int32_t* qdocl = (int32_t*)(smem + L::QDOC);
+__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
+  constexpr int TB = BQ * D * 2;
+  __shared__ __attribute__((aligned(16))) char qb0_[TB];
+  __shared__ __attribute__((aligned(16))) char qb1_[TB];
+  __shared__ __attribute__((aligned(16))) char ob0_[TB];
+  __shared__ __attribute__((aligned(16))) char ob1_[TB];
+  __shared__ __attribute__((aligned(16))) float lb0_[BQ];
+  __shared__ __attribute__((aligned(16))) float lb1_[BQ];
+  __shared__ __attribute__((aligned(16))) float db0_[BQ];
+  __shared__ __attribute__((aligned(16))) float db1_[BQ];
+  __shared__ __attribute__((aligned(16))) int32_t xb0_[BQ];
+  __shared__ __attribute__((aligned(16))) int32_t xb1_[BQ];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hh = lane >> 5;
@@ -120,221 +151,74 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams a) {
   }
   const int32_t qt0 = qlo / BQ;
   const int32_t qt1 = qhi > qlo ? (qhi + BQ - 1) / BQ : qt0;
+  const int G = a.G;
+  const int nitems = (qt1 - qt0) * G;
 
-  // ---- this wave's keys: K, V as B operands; K interleaved into LDS --------
-  const int32_t mykey = min(wk0 + lq, Lk - 1);
-  bf16x8 kf[D / 16], vf[D / 16];
+  auto issue = [&](int it, char* Qd, char* Od, float* Ld, float* Dd, int32_t* Xd) {
+    const int32_t qt = qt0 + it / G;
+    const int head = kvh * G + it % G;
+    tile_load_lds<D, BQ, 4>(Qd, a.q + (int64_t)head * D, a.q_stride, qt * BQ, Lq, wave, lane);
+    tile_load_lds<D, BQ, 4>(Od, a.dout + (int64_t)head * D, (int64_t)a.hq * D, qt * BQ, Lq, wave, lane);
+    const int32_t row = min(qt * BQ + lane, Lq - 1);
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds((const void*)(a.lse + (int64_t)head * a.lse_ld + row), CP_LDS_PTR(Ld), 4, 0, 0);
+    else if (wave == 1)
+      __builtin_amdgcn_global_load_lds((const void*)(a.delta + (int64_t)head * a.lse_ld + row), CP_LDS_PTR(Dd), 4, 0, 0);
+    else if (wave == 2 && docs)
+      __builtin_amdgcn_global_load_lds((const void*)(qs.doc + row), CP_LDS_PTR(Xd), 4, 0, 0);
+  };
+  if (nitems > 0) issue(0, qb0_, ob0_, lb0_, db0_, xb0_);
+
+  KvState<D> st;
   {
+    const int32_t mykey = min(wk0 + lq, Lk - 1);
     const bf16x8* ksrc = (const bf16x8*)(a.k + (int64_t)mykey * a.kv_stride + (int64_t)kvh * D + hh * 8);
     const bf16x8* vsrc = (const bf16x8*)(a.v + (int64_t)mykey * a.kv_stride + (int64_t)kvh * D + hh * 8);
 #pragma unroll
     for (int kd = 0; kd < D / 16; ++kd) {
-      kf[kd] = ksrc[kd * 2];
-      vf[kd] = vsrc[kd * 2];
+      st.kf[kd] = ksrc[kd * 2];
+      st.vf[kd] = vsrc[kd * 2];
     }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) { st.dka[db] = f32x16{}; st.dva[db] = f32x16{}; }
+    st.qlim = causal ? span_count_lt(qs, span_pos(ks, mykey)) : 0;
+    st.kdoc = docs ? ks.doc[mykey] : 0;
+    st.kvalid = wk0 + lq < Lk;
   }
-  const int64_t mykpos = span_pos(ks, mykey);
-  const int32_t mykdoc = docs ? ks.doc[mykey] : 0;
-  {
-    constexpr int ITEMS = (BKG / 4) * (D / 8);
-    for (int item = tid; item < ITEMS; item += 256) {
-      int rg = item / (D / 8), dg = item % (D / 8);
-      u32x4 r[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        int32_t row = min(k0 + rg * 4 + x, Lk - 1);
-        r[x] = *(const u32x4*)(a.k + (int64_t)row * a.kv_stride + (int64_t)kvh * D + dg * 8);
-      }
-      store_interleaved(Ki, D, rg, dg, r);
-    }
-  }
+  // wave-uniform bounds: queries >= q_all see all of the wave's keys, queries
+  // < q_none see none of them (causally)
+  const int32_t wlast = wave_has_keys ? wk1 - 1 : Lk - 1;
+  const int32_t q_none = causal ? span_count_lt(qs, span_pos(ks, wave_has_keys ? wk0 : Lk - 1)) : 0;
+  const int32_t q_all = causal ? span_count_lt(qs, span_pos(ks, wlast)) : 0;
+  const int32_t kd_lo = docs ? ks.doc[wave_has_keys ? wk0 : Lk - 1] : 0;
+  const int32_t kd_hi = docs ? ks.doc[wlast] : 0;
+  const float c = a.scale * LOG2E;
 
-  f32x16 dva[D / 32], dka[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) { dva[db] = f32x16{}; dka[db] = f32x16{}; }
-
-  // ---- staging of one (query tile, head) item ------------------------------
-  constexpr int SITEMS = (BQ / 4) * (D / 8);           // 4 rows x 8 dims each
-  constexpr int SI_PER_T = (SITEMS + 255) / 256;
-  u32x4 qreg[SI_PER_T][4], oreg[SI_PER_T][4];
-  float lreg = 0.f, dreg = 0.f;
-  int32_t docreg = 0;
-  const int nitems = (qt1 - qt0) * a.G;
-
-  auto load_item = [&](int it) {
-    const int32_t qt = qt0 + it / a.G;
-    const int head = kvh * a.G + it % a.G;
-    const int32_t base = qt * BQ;
-#pragma unroll
-    for (int i = 0; i < SI_PER_T; ++i) {
-      int item = tid + i * 256;
-      if (item < SITEMS) {
-        int rg = item / (D / 8), dg = item % (D / 8);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          int32_t row = min(base + rg * 4 + x, Lq - 1);
-          qreg[i][x] = *(const u32x4*)(a.q + (int64_t)row * a.q_stride + (int64_t)head * D + dg * 8);
-          oreg[i][x] = *(const u32x4*)(a.dout + ((int64_t)row * a.hq + head) * D + dg * 8);
-        }
-      }
-    }
-    if (tid < BQ) {
-      int32_t row = min(base + tid, Lq - 1);
-      lreg = a.lse[(int64_t)head * a.lse_ld + row];
-      dreg = a.delta[(int64_t)head * a.lse_ld + row];
-      docreg = docs ? qs.doc[row] : 0;
-    }
-  };
-  auto store_item = [&]() {
-#pragma unroll
-    for (int i = 0; i < SI_PER_T; ++i) {
-      int item = tid + i * 256;
-      if (item < SITEMS) {
-        int rg = item / (D / 8), dg = item % (D / 8);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          *(u32x4*)(Qr + (rg * 4 + x) * L::RST + dg * 8) = qreg[i][x];
-          *(u32x4*)(dOr + (rg * 4 + x) * L::RST + dg * 8) = oreg[i][x];
-        }
-        store_interleaved(Qi, D, rg, dg, qreg[i]);
-        store_interleaved(dOi, D, rg, dg, oreg[i]);
-      }
-    }
-    if (tid < BQ) {
-      lse2[tid] = (lreg == -INFINITY) ? INFINITY : lreg * LOG2E;
-      dlt[tid] = dreg;
-      qdocl[tid] = docreg;
-    }
-  };
-
-  if (nitems > 0) {
-    load_item(0);
-    store_item();
-  }
+  wait_vm0();
   __syncthreads();
 
-  const float c = a.scale * LOG2E;
-  for (int it = 0; it < nitems; ++it) {
-    const int32_t qt = qt0 + it / a.G;
-    const int head = kvh * a.G + it % a.G;
-    const int32_t qa0 = qt * BQ, qa1 = min(Lq, qa0 + BQ);
-    if (it + 1 < nitems) load_item(it + 1);
-
-    const int wg_cls = block_class(qs, qa0, qa1, ks, k0, k1, causal);
-    const int cls = (wave_has_keys && wg_cls != TILE_SKIP)
-                        ? block_class(qs, qa0, qa1, ks, wk0, wk1, causal) : TILE_SKIP;
-
-    if (cls != TILE_SKIP) {
-      f32x16 s[2], dp[2];
-      s[0] = s[1] = dp[0] = dp[1] = f32x16{};
-#pragma unroll
-      for (int kd = 0; kd < D / 16; ++kd) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          bf16x8 qa = *(const bf16x8*)(Qr + (qb * 32 + lq) * L::RST + kd * 16 + hh * 8);
-          bf16x8 oa = *(const bf16x8*)(dOr + (qb * 32 + lq) * L::RST + kd * 16 + hh * 8);
-          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kd], s[qb], 0, 0, 0);
-          dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kd], dp[qb], 0, 0, 0);
-        }
-      }
-      const bool need_mask = cls == TILE_PARTIAL || qa1 - qa0 < BQ || wk1 - wk0 < BKW;
-      const bool key_ok = wk0 + lq < wk1;
-      bf16x8 pf[4], dsf[4];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qr = qb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-          float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -lse2[qr]));
-          if (need_mask) {
-            const int32_t qidx = qa0 + qr;
-            bool ok = key_ok && qidx < qa1 && (!causal || mykpos <= span_pos(qs, qidx)) &&
-                      (!docs || qdocl[qr] == mykdoc);
-            if (!ok) p = 0.f;
-          }
-          const float ds = p * (dp[qb][r] - dlt[qr]) * a.scale;
-          const int t = qb * 2 + (r >> 3), sl = r & 7;
-          pf[t][sl] = (__bf16)p;
-          dsf[t][sl] = (__bf16)ds;
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int d = db * 32 + lq;
-          bf16x8 oa = read_interleaved(dOi, D, t, hh, d);
-          bf16x8 qa = read_interleaved(Qi, D, t, hh, d);
-          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pf[t], dva[db], 0, 0, 0);
-          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsf[t], dka[db], 0, 0, 0);
-        }
-      }
-      // dS (bf16) to LDS, [query][key] row-major, for the dQ product
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-          const int qr = t * 16 + (sl >> 2) * 8 + hh * 4 + (sl & 3);
-          dSl[qr * L::DSST + wave * BKW + lq] = dsf[t][sl];
-        }
-    } else if (wg_cls != TILE_SKIP) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-          const int qr = t * 16 + (sl >> 2) * 8 + hh * 4 + (sl & 3);
-          dSl[qr * L::DSST + wave * BKW + lq] = (__bf16)0.f;
-        }
+  auto step = [&](int it, const char* Qc, const char* Oc, const float* Lc, const float* Dc, const int32_t* Xc,
+                  char* Qn, char* On, float* Ln, float* Dn, int32_t* Xn) {
+    if (it + 1 < nitems) issue(it + 1, Qn, On, Ln, Dn, Xn);
+    const int32_t qa0 = (qt0 + it / G) * BQ, qa1 = min(Lq, qa0 + BQ);
+    bool live = wave_has_keys && qa1 - 1 >= q_none;
+    bool full = qa1 - qa0 == BQ && qa0 >= q_all && wk1 - wk0 == BKW;
+    if (docs) {
+      const int32_t qd_lo = Xc[0], qd_hi = Xc[qa1 - qa0 - 1];
+      live = live && kd_hi >= qd_lo && kd_lo <= qd_hi;
+      full = full && qd_lo == qd_hi && kd_lo == kd_hi && kd_lo == qd_lo;
     }
+    if (live) dkdv_tile<D>(st, Qc, Oc, Lc, Dc, Xc, qa0, Lq, !full, docs, c, a.scale, lane);
+    wait_vm0();
     __syncthreads();
-
-    if (wg_cls != TILE_SKIP) {
-      // dQ^T (32 d rows x 32 queries per block) = K^T dS^T over the 128 keys.
-      // The (d block, query block) pairs are split over the 4 waves: D=128 has
-      // 4 x 2 pairs (wave w: d block w, both query blocks), D=64 has 2 x 2
-      // (wave w: d block w/2, query block w%2).
-      constexpr int QBW = D / 64;                 // query blocks per wave
-      const int dblk = D == 128 ? wave : (wave >> 1);
-      const int qbb = D == 128 ? 0 : (wave & 1);
-      f32x16 dq[QBW];
-#pragma unroll
-      for (int x = 0; x < QBW; ++x) dq[x] = f32x16{};
-      const int d = dblk * 32 + lq;
-#pragma unroll
-      for (int t = 0; t < BKG / 16; ++t) {
-        // natural slot order: slot s <-> key 16t + 8hh + s, for A and B alike
-        u32x2 lo = *(const u32x2*)(Ki + ((4 * t + 2 * hh) * D + d) * 4);
-        u32x2 hi = *(const u32x2*)(Ki + ((4 * t + 2 * hh + 1) * D + d) * 4);
-        u32x4 kv = {lo.x, lo.y, hi.x, hi.y};
-        bf16x8 ka = __builtin_bit_cast(bf16x8, kv);
-#pragma unroll
-        for (int x = 0; x < QBW; ++x) {
-          const int qb = qbb + x;
-          bf16x8 db8 = *(const bf16x8*)(dSl + (qb * 32 + lq) * L::DSST + t * 16 + hh * 8);
-          dq[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, db8, dq[x], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int x = 0; x < QBW; ++x) {
-        const int32_t row = qa0 + (qbb + x) * 32 + lq;
-        if (row < qa1) {
-          float* dst = a.dq + ((int64_t)row * a.hq + head) * D + dblk * 32 + hh * 4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) atomicAdd(dst + j * 8 + i, dq[x][4 * j + i]);
-        }
-      }
-    }
-    __syncthreads();
-    if (it + 1 < nitems) {
-      store_item();
-      __syncthreads();
-    }
+  };
+  for (int it = 0; it < nitems; it += 2) {
+    step(it, qb0_, ob0_, lb0_, db0_, xb0_, qb1_, ob1_, lb1_, db1_, xb1_);
+    if (it + 1 < nitems) step(it + 1, qb1_, ob1_, lb1_, db1_, xb1_, qb0_, ob0_, lb0_, db0_, xb0_);
   }
 
   // ---- dK, dV (exclusive to this work-group): read-modify-write -------------
-  if (wave_has_keys && wk0 + lq < wk1) {
+  if (st.kvalid && wave_has_keys) {
     const int64_t base = ((int64_t)(wk0 + lq) * a.hkv + kvh) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -344,30 +228,222 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams a) {
         f32x4* pk = (f32x4*)(a.dk + base + d);
         f32x4* pv = (f32x4*)(a.dv + base + d);
         f32x4 ok = *pk, ov = *pv;
-        ok[0] += dka[db][4 * j]; ok[1] += dka[db][4 * j + 1];
-        ok[2] += dka[db][4 * j + 2]; ok[3] += dka[db][4 * j + 3];
-        ov[0] += dva[db][4 * j]; ov[1] += dva[db][4 * j + 1];
-        ov[2] += dva[db][4 * j + 2]; ov[3] += dva[db][4 * j + 3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ok[i] += st.dka[db][4 * j + i];
+          ov[i] += st.dva[db][4 * j + i];
+        }
         *pk = ok;
         *pv = ov;
       }
   }
 }
 
+// ================================= dQ =======================================
+
+template <int D>
+struct QState {
+  bf16x8 qf[2][D / 16];     // B operands: 64 query rows
+  bf16x8 of[2][D / 16];     // B operands: their dO rows
+  f32x16 acc[2][D / 32];    // dQ^T accumulators [query block][d block]
+  float nl[2];              // -LSE * log2(e) of the lane's query column
+  float dl[2];              // Delta of the lane's query column
+  int32_t lim[2];           // keys [0, lim) are causally visible (and < Lk)
+  int32_t qdoc[2];
+};
+
+template <int D>
+__device__ inline void dq_tile(QState<D>& st, const char* Kt, const char* Vt, const int32_t* Dt, int32_t kb0,
+                               bool mask, bool docs, float c, float scale, int lane) {
+  const int lq = lane & 31, hh = lane >> 5;
+  const int s16 = lane & 15, cg = (lane >> 4) & 1;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kd = 0; kd < D / 16; ++kd) {
+      const bf16x8 ka = lds_row8<D>(Kt, kb * 32 + lq, kd * 16 + hh * 8);
+      const bf16x8 va = lds_row8<D>(Vt, kb * 32 + lq, kd * 16 + hh * 8);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[qb][kd], s[qb], 0, 0, 0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, st.of[qb][kd], dp[qb], 0, 0, 0);
+      }
+    }
+    // element r of block qb: query = lane's column of block qb, key = kb*32 + 8(r/4) + 4hh + r%4
+    bf16x8 dsf[2][2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+      const int32_t kd_ = Dt[kk];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, st.nl[qb]));
+        if (mask) {
+          const bool ok = (kb0 + kk < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
+          p = ok ? p : 0.f;
+        }
+        dsf[qb][r >> 3][r & 7] = (__bf16)(p * (dp[qb][r] - st.dl[qb]) * scale);
+      }
+    }
+    // dQ^T[qb][db] += K^T (d rows, 16 keys per step) x dS^T
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int k0 = kb * 32 + 16 * t;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int c0 = db * 32 + 16 * cg;
+        const bf16x8 ka = cat8(lds_tr4<D>(Kt, k0 + 4 * hh, c0, s16), lds_tr4<D>(Kt, k0 + 8 + 4 * hh, c0, s16));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          st.acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsf[qb][t], st.acc[qb][db], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
+  constexpr int TB = BK * D * 2;
+  __shared__ __attribute__((aligned(16))) char kb0_[TB];
+  __shared__ __attribute__((aligned(16))) char kb1_[TB];
+  __shared__ __attribute__((aligned(16))) char vb0_[TB];
+  __shared__ __attribute__((aligned(16))) char vb1_[TB];
+  __shared__ __attribute__((aligned(16))) int32_t xb0_[BK];
+  __shared__ __attribute__((aligned(16))) int32_t xb1_[BK];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lq = lane & 31, hh = lane >> 5;
+
+  const int32_t w = xcd_remap(blockIdx.x, gridDim.x);
+  if (w >= a.n_work) return;
+  const int32_t grp = w / a.nqt;
+  const int32_t qt = a.nqt - 1 - (w % a.nqt);          // heavy first
+  const int hpw = a.heads_per_wg;
+  const int groups_per_kv = a.G / hpw;
+  const int kvh = grp / groups_per_kv;
+  const int head = kvh * a.G + (grp % groups_per_kv) * hpw + (wave % hpw);
+  const int qblk = wave / hpw;
+
+  const SpanD qs = a.qs, ks = a.ks;
+  const int32_t Lq = span_len(qs), Lk = span_len(ks);
+  const bool causal = a.causal != 0;
+  const bool docs = qs.doc != nullptr;
+  const int32_t wg_q0 = qt * BQ * a.qblocks_per_wg;
+  const int32_t wg_q1 = min(Lq, wg_q0 + BQ * a.qblocks_per_wg);
+  const int32_t q0 = wg_q0 + qblk * BQ;
+  const bool wave_live = q0 < Lq;
+  const int32_t q1 = min(Lq, q0 + BQ);
+
+  int32_t klo = 0, khi = Lk;
+  if (causal) khi = span_count_le(ks, span_pos(qs, wg_q1 - 1));
+  if (docs) {
+    klo = wave_lower_bound(ks.doc, Lk, qs.doc[wg_q0]);
+    khi = min(khi, wave_lower_bound(ks.doc, Lk, qs.doc[wg_q1 - 1] + 1));
+  }
+  const int32_t kt0 = klo / BK;
+  const int32_t kt1 = khi > klo ? (khi + BK - 1) / BK : kt0;
+
+  const __bf16* kbase = a.k + (int64_t)kvh * D;
+  const __bf16* vbase = a.v + (int64_t)kvh * D;
+  auto issue = [&](int32_t t, char* Kd, char* Vd, int32_t* Xd) {
+    tile_load_lds<D, BK, 4>(Kd, kbase, a.kv_stride, t * BK, Lk, wave, lane);
+    tile_load_lds<D, BK, 4>(Vd, vbase, a.kv_stride, t * BK, Lk, wave, lane);
+    if (docs && wave == 0) {
+      const int32_t row = min(t * BK + lane, Lk - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(ks.doc + row), CP_LDS_PTR(Xd), 4, 0, 0);
+    }
+  };
+  if (kt0 < kt1) issue(kt0, kb0_, vb0_, xb0_);
+
+  QState<D> st;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int32_t row = min(q0 + qb * 32 + lq, Lq - 1);
+    const bf16x8* qsrc = (const bf16x8*)(a.q + (int64_t)row * a.q_stride + (int64_t)head * D + hh * 8);
+    const bf16x8* osrc = (const bf16x8*)(a.dout + ((int64_t)row * a.hq + head) * D + hh * 8);
+#pragma unroll
+    for (int kd = 0; kd < D / 16; ++kd) {
+      st.qf[qb][kd] = qsrc[kd * 2];
+      st.of[qb][kd] = osrc[kd * 2];
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) st.acc[qb][db] = f32x16{};
+    st.nl[qb] = -a.lse[(int64_t)head * a.lse_ld + row] * LOG2E;
+    st.dl[qb] = a.delta[(int64_t)head * a.lse_ld + row];
+    st.lim[qb] = causal ? min(Lk, span_count_le(ks, span_pos(qs, row))) : Lk;
+    st.qdoc[qb] = docs ? qs.doc[row] : 0;
+  }
+  const int32_t lim_lo = causal ? min(Lk, span_count_le(ks, span_pos(qs, q0 < Lq ? q0 : Lq - 1))) : Lk;
+  const int32_t lim_hi = causal ? min(Lk, span_count_le(ks, span_pos(qs, q1 - 1))) : Lk;
+  const int32_t qd_lo = docs ? qs.doc[q0 < Lq ? q0 : Lq - 1] : 0;
+  const int32_t qd_hi = docs ? qs.doc[q1 - 1] : 0;
+  const float c = a.scale * LOG2E;
+
+  wait_vm0();
+  __syncthreads();
+
+  auto step = [&](int32_t t, const char* Kc, const char* Vc, const int32_t* Xc, char* Kn, char* Vn, int32_t* Xn) {
+    if (t + 1 < kt1) issue(t + 1, Kn, Vn, Xn);
+    const int32_t kb0 = t * BK, kb1 = min(Lk, kb0 + BK);
+    bool live = wave_live && kb0 < lim_hi;
+    bool full = kb1 - kb0 == BK && kb1 <= lim_lo;
+    if (docs) {
+      const int32_t kd_lo = Xc[0], kd_hi = Xc[kb1 - kb0 - 1];
+      live = live && kd_hi >= qd_lo && kd_lo <= qd_hi;
+      full = full && qd_lo == qd_hi && kd_lo == kd_hi && kd_lo == qd_lo;
+    }
+    if (live) dq_tile<D>(st, Kc, Vc, Xc, kb0, !full, docs, c, a.scale, lane);
+    wait_vm0();
+    __syncthreads();
+  };
+  for (int32_t t = kt0; t < kt1; t += 2) {
+    step(t, kb0_, vb0_, xb0_, kb1_, vb1_, xb1_);
+    if (t + 1 < kt1) step(t + 1, kb1_, vb1_, xb1_, kb0_, vb0_, xb0_);
+  }
+
+  if (!wave_live) return;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int32_t row = q0 + qb * 32 + lq;
+    if (row < Lq) {
+      float* dst = a.dq + ((int64_t)row * a.hq + head) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4* p = (f32x4*)(dst + db * 32 + j * 8 + hh * 4);
+          f32x4 v = *p;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] += st.acc[qb][db][4 * j + i];
+          *p = v;
+        }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+  if (span_len(p.qs) == 0 || span_len(p.ks) == 0) return hipSuccess;
   BwdParams a = p;
-  const int32_t Lk = span_len(a.ks);
+  const int32_t Lk = span_len(a.ks), Lq = span_len(a.qs);
   a.nkt = (Lk + BKG - 1) / BKG;
   a.n_work = a.nkt * a.hkv;
-  if (a.n_work == 0 || span_len(a.qs) == 0) return hipSuccess;
-  const int32_t grid = round_up8(a.n_work);
-  if (a.d == 128) {
-    hipLaunchKernelGGL(bwd_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(bwd_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, a);
-  }
+  int32_t grid = round_up8(a.n_work);
+  if (a.d == 128) hipLaunchKernelGGL(dkdv_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(dkdv_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  BwdParams b = p;
+  b.heads_per_wg = b.G >= 4 ? 4 : b.G;
+  b.qblocks_per_wg = 4 / b.heads_per_wg;
+  b.nqt = (Lq + BQ * b.qblocks_per_wg - 1) / (BQ * b.qblocks_per_wg);
+  b.n_work = b.nqt * (b.hq / b.heads_per_wg);
+  grid = round_up8(b.n_work);
+  if (b.d == 128) hipLaunchKernelGGL(dq_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, b);
+  else hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, b);
   return hipGetLastError();
 }
 

@@ -13,30 +13,30 @@
 //     head.  With grouped-query attention the 4 waves of a group take 4 query
 //     heads that read the same KV head (or 2 heads x 2 row blocks, or 1 head x
 //     4 row blocks), so every K/V tile staged in LDS feeds 4 waves.
-//   * keys stream through LDS in tiles of 64, double-buffered: the next tile's
-//     global loads are issued before the current tile's MFMAs.
+//   * keys stream through LDS in tiles of 64 rows, double-buffered, copied
+//     with direct-to-LDS loads issued one tile ahead (tile_io.h).
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the K tile is the A operand
-//     (read from LDS), the wave's Q rows are the B operand (held in VGPRs for
-//     the whole kernel).  In the 32x32 accumulator each lane holds one query
-//     column and 16 key rows, so the softmax row statistics need one cross-lane
-//     exchange (lane ^ 32) per tile.
+//     (ds_read_b128), the wave's Q rows are the B operand (in VGPRs for the
+//     whole kernel).  Each lane holds one query column and 16 key rows of the
+//     32x32 accumulator, so a row's statistics need one cross-lane exchange.
 //   * O^T += V^T P^T: P^T goes from the S^T accumulator straight into the B
-//     operand (no LDS round trip).  V is stored in LDS interleaved by groups of
-//     4 keys ([key/4][d][4]) so the A operand of each lane is two 8-byte reads.
+//     operand; V^T is read with the LDS transpose read ds_read_b64_tr_b16.
+//   * softmax in base 2 with the scale folded into one FMA; the running max
+//     is raised only when a tile's max exceeds it by more than 2^8 (the
+//     accumulators are then rescaled), which is exact and makes rescaling
+//     rare.
 //   * fully masked tiles (causal or document) are skipped; the element mask is
 //     evaluated only on partial tiles and on the ragged last tile.
 //   * work-groups run heavy-first (later query tiles have more causal work),
 //     remapped so each XCD works on a contiguous range of KV heads.
 #include "common.h"
 #include "kernels.h"
+#include "tile_io.h"
 
 namespace cp {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -44,31 +44,124 @@ constexpr int BK = 64;      // keys per tile
 constexpr int QW = 64;      // query rows per wave
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr float RESCALE_LOG2 = 8.0f;   // lazy rescale threshold (base-2 units)
+
+__device__ inline void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int D>
-struct Lds {
-  static constexpr int KST = D + 8;                 // padded K row (elements)
-  static constexpr int KBYTES = BK * KST * 2;
-  static constexpr int VBYTES = BK * D * 2;
-  static constexpr int STAGE = KBYTES + VBYTES + BK * 4;   // + key doc ids
-  static constexpr int TOTAL = 2 * STAGE;
+struct FwdState {
+  bf16x8 qf[2][D / 16];     // B operands: this wave's 64 query rows
+  f32x16 oacc[2][D / 32];   // O^T accumulators [query block][d block]
+  float mrow[2];            // running max (raw score units), per query block
+  float lrow[2];            // this lane's share of the row sum
+  int32_t lim[2];           // keys [0, lim) are causally visible (and < Lk)
+  int32_t qdoc[2];
 };
 
-__device__ inline bf16x8 cvt8(const f32x16& s, int base, float c, float moff, float& sum) {
-  bf16x8 r;
+// Element mask of a partial or ragged half-tile (32 keys from kh0).  Positions
+// increase along local order, so "key position <= query position" is
+// "key index < lim".
+template <int D>
+__device__ inline void fwd_mask(const FwdState<D>& st, f32x16 (&s)[2], const int32_t* Dt, int32_t kb0,
+                                int kh0, bool docs, int hh) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float p = __builtin_amdgcn_exp2f(fmaf(s[base + i], c, moff));
-    sum += p;
-    r[i] = (__bf16)p;
+  for (int r = 0; r < 16; ++r) {
+    const int kk = kh0 + (r >> 2) * 8 + hh * 4 + (r & 3);
+    const int32_t kidx = kb0 + kk;
+    const int32_t kd_ = Dt[kk];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const bool ok = (kidx < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
+      s[qb][r] = ok ? s[qb][r] : -INFINITY;
+    }
   }
-  return r;
+}
+
+// One 64-key tile for one wave, as two 32-key halves: scores, mask, online
+// softmax, O += P V.
+template <int D>
+__device__ inline void fwd_tile(FwdState<D>& st, const char* Kt, const char* Vt, const int32_t* Dt,
+                                int32_t kb0, bool mask, bool docs, float c, int lane) {
+  const int lq = lane & 31, hh = lane >> 5;
+  const int s16 = lane & 15, cg = (lane >> 4) & 1;
+  const float thr = RESCALE_LOG2 / c;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    // S^T[qb]: keys kb*32.. (rows) x queries qb*32.. (columns)
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kd = 0; kd < D / 16; ++kd) {
+      const bf16x8 ka = lds_row8<D>(Kt, kb * 32 + lq, kd * 16 + hh * 8);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[qb][kd], s[qb], 0, 0, 0);
+    }
+    if (mask) fwd_mask<D>(st, s, Dt, kb0, kb * 32, docs, hh);
+
+    float mx[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float m0 = fmaxf(s[qb][0], s[qb][1]);
+#pragma unroll
+      for (int r = 2; r < 16; r += 2) m0 = fmaxf(m0, fmaxf(s[qb][r], s[qb][r + 1]));
+      mx[qb] = fmaxf(m0, __shfl_xor(m0, 32));
+    }
+    // raise the running max only when the block exceeds it by > 2^8
+    const bool grow = (mx[0] > st.mrow[0] + thr) | (mx[1] > st.mrow[1] + thr);
+    if (__builtin_expect(__any(grow), 0)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float mn = fmaxf(st.mrow[qb], mx[qb]);
+        const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((st.mrow[qb] - mn) * c);
+        st.lrow[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) st.oacc[qb][db] *= alpha;
+        st.mrow[qb] = mn;
+      }
+    }
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float moff = (st.mrow[qb] == -INFINITY) ? 0.f : -st.mrow[qb] * c;
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][t * 8 + i], c, moff));
+          sum += p;
+          pf[qb][t][i] = (__bf16)p;
+        }
+      }
+      st.lrow[qb] += sum;
+    }
+
+    // O^T[qb][db] += V^T (d rows db*32.., 16 keys per step) x P^T
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int k0 = kb * 32 + 16 * t;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int c0 = db * 32 + 16 * cg;
+        const bf16x8 va = cat8(lds_tr4<D>(Vt, k0 + 4 * hh, c0, s16),
+                               lds_tr4<D>(Vt, k0 + 8 + 4 * hh, c0, s16));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          st.oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][t], st.oacc[qb][db], 0, 0, 0);
+      }
+    }
+  }
 }
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
-  using L = Lds<D>;
-  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  constexpr int TB = BK * D * 2;     // bytes of one K or V tile
+  __shared__ __attribute__((aligned(16))) char kb0_[TB];
+  __shared__ __attribute__((aligned(16))) char kb1_[TB];
+  __shared__ __attribute__((aligned(16))) char vb0_[TB];
+  __shared__ __attribute__((aligned(16))) char vb1_[TB];
+  __shared__ __attribute__((aligned(16))) int32_t db0_[BK];
+  __shared__ __attribute__((aligned(16))) int32_t db1_[BK];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hh = lane >> 5;
@@ -93,222 +186,86 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
   const bool wave_live = q0 < Lq;
   const int32_t q1 = min(Lq, q0 + QW);
 
-  // ---- key range of the work-group -------------------------------------
+  // ---- key range of the work-group ------------------------------------
   int32_t klo = 0, khi = Lk;
   if (causal) khi = span_count_le(ks, span_pos(qs, wg_q1 - 1));
   if (docs) {
     klo = wave_lower_bound(ks.doc, Lk, qs.doc[wg_q0]);
-    int32_t hi2 = wave_lower_bound(ks.doc, Lk, qs.doc[wg_q1 - 1] + 1);
-    khi = min(khi, hi2);
+    khi = min(khi, wave_lower_bound(ks.doc, Lk, qs.doc[wg_q1 - 1] + 1));
   }
   const int32_t kt0 = klo / BK;
   const int32_t kt1 = khi > klo ? (khi + BK - 1) / BK : kt0;
 
+  const __bf16* kbase = a.k + (int64_t)kvh * D;
+  const __bf16* vbase = a.v + (int64_t)kvh * D;
+  auto issue = [&](int32_t kt, char* Kd, char* Vd, int32_t* Dd) {
+    tile_load_lds<D, BK, 4>(Kd, kbase, a.kv_stride, kt * BK, Lk, wave, lane);
+    tile_load_lds<D, BK, 4>(Vd, vbase, a.kv_stride, kt * BK, Lk, wave, lane);
+    if (docs && wave == 0) {
+      const int32_t row = min(kt * BK + lane, Lk - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(ks.doc + row), CP_LDS_PTR(Dd), 4, 0, 0);
+    }
+  };
+  if (kt0 < kt1) issue(kt0, kb0_, vb0_, db0_);
+
   // ---- this wave's Q rows as MFMA B operands ----------------------------
-  bf16x8 qf[2][D / 16];
-  int64_t qpos_l[2];
-  int32_t qdoc_l[2];
+  FwdState<D> st;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    int32_t row = min(q0 + qb * 32 + lq, Lq - 1);
+    const int32_t row = min(q0 + qb * 32 + lq, Lq - 1);
     const bf16x8* src = (const bf16x8*)(a.q + (int64_t)row * a.q_stride + (int64_t)head * D + hh * 8);
 #pragma unroll
-    for (int kd = 0; kd < D / 16; ++kd) qf[qb][kd] = src[kd * 2];
-    qpos_l[qb] = span_pos(qs, row);
-    qdoc_l[qb] = docs ? qs.doc[row] : 0;
+    for (int kd = 0; kd < D / 16; ++kd) st.qf[qb][kd] = src[kd * 2];
+    st.lim[qb] = causal ? min(Lk, span_count_le(ks, span_pos(qs, row))) : Lk;
+    st.qdoc[qb] = docs ? qs.doc[row] : 0;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) st.oacc[qb][db] = f32x16{};
+    st.mrow[qb] = -INFINITY;
+    st.lrow[qb] = 0.f;
   }
-
-  f32x16 oacc[2][D / 32];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
-  float mrow[2] = {-INFINITY, -INFINITY};   // running max of raw scores
-  float lrow[2] = {0.f, 0.f};               // this lane's share of the row sum
   const float c = a.scale_log2;              // scale * log2(e)
 
-  // ---- global -> register staging of one K/V tile -----------------------
-  // K: 64 rows x D, 16-byte pieces, row-major into LDS (padded rows).
-  // V: each thread takes 4 consecutive keys x 8 dims and writes 8 pieces of
-  //    4 keys (8 bytes) into the [key/4][d][4] layout.
-  constexpr int KPIECES = BK * D / 8;                 // 16-byte pieces per K tile
-  constexpr int KP_PER_T = KPIECES / 256;             // 4 (D=128) or 2 (D=64)
-  constexpr int VITEMS = (BK / 4) * (D / 8);          // (4 keys x 8 dims) items
-  constexpr int VI_PER_T = (VITEMS + 255) / 256;      // 1
-  u32x4 kreg[KP_PER_T];
-  u32x4 vreg[VI_PER_T][4];
-  int32_t dreg = 0;
-
-  auto load_tile = [&](int32_t kt) {
-    const int32_t base = kt * BK;
-#pragma unroll
-    for (int i = 0; i < KP_PER_T; ++i) {
-      int piece = tid + i * 256;
-      int key = piece / (D / 8), col = (piece % (D / 8)) * 8;
-      int32_t row = min(base + key, Lk - 1);
-      kreg[i] = *(const u32x4*)(a.k + (int64_t)row * a.kv_stride + (int64_t)kvh * D + col);
-    }
-#pragma unroll
-    for (int i = 0; i < VI_PER_T; ++i) {
-      int item = tid + i * 256;
-      if (item < VITEMS) {
-        int kg = item / (D / 8), dg = item % (D / 8);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int32_t row = min(base + kg * 4 + r, Lk - 1);
-          vreg[i][r] = *(const u32x4*)(a.v + (int64_t)row * a.kv_stride + (int64_t)kvh * D + dg * 8);
-        }
-      }
-    }
-    if (docs && tid < BK) dreg = ks.doc[min(base + tid, Lk - 1)];
-  };
-  auto store_tile = [&](int stage) {
-    char* st = smem + stage * L::STAGE;
-    __bf16* Ks = (__bf16*)st;
-    __bf16* Vs = (__bf16*)(st + L::KBYTES);
-    int32_t* Ds = (int32_t*)(st + L::KBYTES + L::VBYTES);
-#pragma unroll
-    for (int i = 0; i < KP_PER_T; ++i) {
-      int piece = tid + i * 256;
-      int key = piece / (D / 8), col = (piece % (D / 8)) * 8;
-      *(u32x4*)(Ks + key * L::KST + col) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VI_PER_T; ++i) {
-      int item = tid + i * 256;
-      if (item < VITEMS) {
-        int kg = item / (D / 8), dg = item % (D / 8);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {        // dword m holds dims 2m, 2m+1
-          u32x2 lo, hi;
-          lo.x = __builtin_amdgcn_perm(vreg[i][1][m], vreg[i][0][m], 0x05040100u);
-          lo.y = __builtin_amdgcn_perm(vreg[i][3][m], vreg[i][2][m], 0x05040100u);
-          hi.x = __builtin_amdgcn_perm(vreg[i][1][m], vreg[i][0][m], 0x07060302u);
-          hi.y = __builtin_amdgcn_perm(vreg[i][3][m], vreg[i][2][m], 0x07060302u);
-          int d0 = dg * 8 + 2 * m;
-          *(u32x2*)(Vs + ((kg * D) + d0) * 4) = lo;
-          *(u32x2*)(Vs + ((kg * D) + d0 + 1) * 4) = hi;
-        }
-      }
-    }
-    if (docs && tid < BK) Ds[tid] = dreg;
-  };
-
-  if (kt0 < kt1) {
-    load_tile(kt0);
-    store_tile(0);
-  }
+  wait_vm0();
   __syncthreads();
 
-  for (int32_t kt = kt0; kt < kt1; ++kt) {
-    const int stage = (kt - kt0) & 1;
-    if (kt + 1 < kt1) load_tile(kt + 1);
+  // wave-uniform bounds for classifying tiles: keys [0, lim_lo) are visible to
+  // every row of the wave, keys >= lim_hi to none; doc ids of the first and
+  // last row
+  const int32_t lim_lo = causal ? min(Lk, span_count_le(ks, span_pos(qs, q0 < Lq ? q0 : Lq - 1))) : Lk;
+  const int32_t lim_hi = causal ? min(Lk, span_count_le(ks, span_pos(qs, q1 - 1))) : Lk;
+  const int32_t qd_lo = docs ? qs.doc[q0 < Lq ? q0 : Lq - 1] : 0;
+  const int32_t qd_hi = docs ? qs.doc[q1 - 1] : 0;
 
+  auto step = [&](int32_t kt, const char* Kc, const char* Vc, const int32_t* Dc, char* Kn, char* Vn,
+                  int32_t* Dn) {
+    if (kt + 1 < kt1) issue(kt + 1, Kn, Vn, Dn);
     const int32_t kb0 = kt * BK, kb1 = min(Lk, kb0 + BK);
-    int cls = wave_live ? block_class(qs, q0, q1, ks, kb0, kb1, causal) : TILE_SKIP;
-    if (cls != TILE_SKIP) {
-      const char* st = smem + stage * L::STAGE;
-      const __bf16* Ks = (const __bf16*)st;
-      const __bf16* Vs = (const __bf16*)(st + L::KBYTES);
-      const int32_t* Ds = (const int32_t*)(st + L::KBYTES + L::VBYTES);
-
-      // S^T[kb][qb]: keys kb*32.. (rows) x queries qb*32.. (columns)
-      f32x16 s[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x16{};
-#pragma unroll
-      for (int kd = 0; kd < D / 16; ++kd) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          bf16x8 ka = *(const bf16x8*)(Ks + (kb * 32 + lq) * L::KST + kd * 16 + hh * 8);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][kd], s[kb][qb], 0, 0, 0);
-        }
-      }
-
-      if (cls == TILE_PARTIAL || kb1 - kb0 < BK) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            int kk = kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-            int32_t kidx = kb0 + kk;
-            bool kin = kidx < kb1;
-            int64_t kp = span_pos(ks, kidx);
-            int32_t kd_ = docs ? Ds[kk] : 0;
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-              bool ok = kin && (!causal || kp <= qpos_l[qb]) && (!docs || kd_ == qdoc_l[qb]);
-              if (!ok) s[kb][qb][r] = -INFINITY;
-            }
-          }
-      }
-
-      // online softmax per query column
-      float mx[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float m0 = s[0][qb][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) m0 = fmaxf(m0, s[0][qb][r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) m0 = fmaxf(m0, s[1][qb][r]);
-        m0 = fmaxf(m0, __shfl_xor(m0, 32));
-        mx[qb] = fmaxf(mrow[qb], m0);
-      }
-      const bool grow = (mx[0] > mrow[0]) || (mx[1] > mrow[1]);
-      if (__any(grow)) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          float alpha = (mx[qb] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((mrow[qb] - mx[qb]) * c);
-          lrow[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
-          mrow[qb] = mx[qb];
-        }
-      }
-      bf16x8 pf[2][4];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float moff = (mrow[qb] == -INFINITY) ? 0.f : -mrow[qb] * c;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) pf[qb][t] = cvt8(s[t >> 1][qb], (t & 1) * 8, c, moff, lrow[qb]);
-      }
-
-      // O^T[qb][db] += V^T (d rows db*32.., 16 keys per step) x P^T
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int d = db * 32 + lq;
-          u32x2 lo = *(const u32x2*)(Vs + ((4 * t + hh) * D + d) * 4);
-          u32x2 hi = *(const u32x2*)(Vs + ((4 * t + 2 + hh) * D + d) * 4);
-          u32x4 av = {lo.x, lo.y, hi.x, hi.y};
-          bf16x8 va = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][t], oacc[qb][db], 0, 0, 0);
-        }
-      }
+    bool live = wave_live && kb0 < lim_hi;
+    bool full = kb1 - kb0 == BK && kb1 <= lim_lo;
+    if (docs) {
+      const int32_t kd_lo = Dc[0], kd_hi = Dc[kb1 - kb0 - 1];
+      live = live && kd_hi >= qd_lo && kd_lo <= qd_hi;
+      full = full && qd_lo == qd_hi && kd_lo == kd_hi && kd_lo == qd_lo;
     }
-
-    if (kt + 1 < kt1) store_tile(stage ^ 1);
+    if (live) fwd_tile<D>(st, Kc, Vc, Dc, kb0, !full, docs, c, lane);
+    wait_vm0();
     __syncthreads();
+  };
+  for (int32_t kt = kt0; kt < kt1; kt += 2) {
+    step(kt, kb0_, vb0_, db0_, kb1_, vb1_, db1_);
+    if (kt + 1 < kt1) step(kt + 1, kb1_, vb1_, db1_, kb0_, vb0_, db0_);
   }
 
   // ---- epilogue -----------------------------------------------------------
   if (!wave_live) return;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float ltot = lrow[qb] + __shfl_xor(lrow[qb], 32);
+    const float ltot = st.lrow[qb] + __shfl_xor(st.lrow[qb], 32);
     const int32_t row = q0 + qb * 32 + lq;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (row < Lq) {
       if (hh == 0) {
-        float lse = ltot > 0.f ? (mrow[qb] * c + __builtin_amdgcn_logf(ltot)) * LN2 : -INFINITY;
+        const float lse = ltot > 0.f ? (st.mrow[qb] * c + __builtin_amdgcn_logf(ltot)) * LN2 : -INFINITY;
         a.lse[(int64_t)head * a.lse_ld + row] = lse;
       }
       const int64_t obase = ((int64_t)row * a.hq + head) * D;
@@ -317,13 +274,12 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = db * 32 + j * 8 + hh * 4;
-          f32x4 v4 = {oacc[qb][db][4 * j] * inv, oacc[qb][db][4 * j + 1] * inv,
-                      oacc[qb][db][4 * j + 2] * inv, oacc[qb][db][4 * j + 3] * inv};
+          const f32x4 v4 = {st.oacc[qb][db][4 * j] * inv, st.oacc[qb][db][4 * j + 1] * inv,
+                            st.oacc[qb][db][4 * j + 2] * inv, st.oacc[qb][db][4 * j + 3] * inv};
           if (a.o_f32) {
             *(f32x4*)((float*)a.o + obase + d) = v4;
           } else {
-            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-            bf16x4 b4 = {(__bf16)v4[0], (__bf16)v4[1], (__bf16)v4[2], (__bf16)v4[3]};
+            const bf16x4 b4 = {(__bf16)v4[0], (__bf16)v4[1], (__bf16)v4[2], (__bf16)v4[3]};
             *(bf16x4*)((__bf16*)a.o + obase + d) = b4;
           }
         }

@@ -8,7 +8,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/cpattn.h"
+#include "cpattn.h"
 #include "kernels.h"
 
 using namespace cp;

@@ -51,6 +51,7 @@ struct BwdParams {
   float* dv;                 // [Lk, hkv, d] +=
   // filled in by the launcher
   int nkt, n_work;
+  int heads_per_wg, qblocks_per_wg, nqt;
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);

@@ -1,0 +1,97 @@
+// LDS tile staging shared by the bf16 MFMA kernels (gfx950).
+//
+// A tile of R rows x D bf16 (row-major in HBM, `stride` elements between
+// rows) is copied HBM -> LDS with direct-to-LDS loads (global_load_lds,
+// 16 bytes per lane; no VGPR round trip).  The LDS image keeps rows whole but
+// permutes each row's 16-byte chunks by an XOR swizzle so that both access
+// patterns the MFMA operands need are free of bank conflicts:
+//   * row reads: 16 lanes each read one 16-byte chunk of 16 consecutive rows
+//     (ds_read_b128, operand with the contraction along d);
+//   * transposed reads: ds_read_b64_tr_b16 over 4 consecutive rows x 16
+//     columns per 16-lane group (operand with the contraction along rows).
+//
+// ds_read_b64_tr_b16 (measured on gfx950): within each 16-lane group, if
+// source lane s reads the 4 consecutive elements M[s][0..3] at its address,
+// destination lane i receives M[4j + i/4][i%4] as element j (j = 0..3).  So
+// when lane s of a group addresses row r0 + s/4, columns c0 + 4(s%4) .. +3,
+// lane i receives column c0 + i of rows r0 .. r0 + 3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define CP_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int D>
+struct Swz {
+  static constexpr int CHUNKS = D / 8;              // 16-byte chunks per row
+  static constexpr int ROW_BYTES = D * 2;
+  // chunk position of chunk c in row r
+  __device__ static inline int pos(int r, int c) {
+    if constexpr (D == 128) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
+    else return c ^ ((r >> 1) & 7);
+  }
+  // byte offset of element (r, col) for an 8-byte aligned col group
+  __device__ static inline int off(int r, int col) {
+    return r * ROW_BYTES + pos(r, col >> 3) * 16 + (col & 4) * 2;
+  }
+};
+
+// Issue the direct-to-LDS loads of an R x D tile whose row i sits at
+// src + row_index(i) * stride (rows past `valid` are clamped to valid-1, so
+// every load is in bounds; callers mask those rows).  NW waves share the
+// work; wave `wave` issues its share.  dst must be 16-byte aligned.
+template <int D, int R, int NW>
+__device__ inline void tile_load_lds(char* dst, const __bf16* src, int64_t stride, int32_t row0,
+                                     int32_t valid_rows, int wave, int lane) {
+  constexpr int CHUNKS = D / 8;
+  constexpr int TOTAL = R * CHUNKS;                  // 16-byte chunks in the tile
+  constexpr int PER_WAVE = TOTAL / (64 * NW);        // instructions per wave
+  static_assert(TOTAL % (64 * NW) == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int slot0 = (wave * PER_WAVE + i) * 64;   // first LDS slot of this instruction
+    const int slot = slot0 + lane;
+    const int r = slot / CHUNKS;
+    const int cpos = slot % CHUNKS;
+    int c = cpos;   // invert the swizzle: the chunk stored at position cpos
+    if constexpr (D == 128) c = cpos ^ (((r & 7) << 1) | ((r >> 3) & 1));
+    else c = cpos ^ ((r >> 1) & 7);
+    int32_t row = row0 + r;
+    row = row < valid_rows ? row : valid_rows - 1;
+    const __bf16* g = src + (int64_t)row * stride + c * 8;
+    __builtin_amdgcn_global_load_lds((const void*)g, CP_LDS_PTR(dst + slot0 * 16), 16, 0, 0);
+  }
+}
+
+// Row read: 8 consecutive elements (16 bytes) of row r starting at column col
+// (a multiple of 8).
+template <int D>
+__device__ inline bf16x8 lds_row8(const char* base, int r, int col) {
+  return *(const bf16x8*)(base + r * Swz<D>::ROW_BYTES + Swz<D>::pos(r, col >> 3) * 16);
+}
+
+// Transposed read for a 16-lane group: this lane (s = lane % 16) addresses
+// row r0 + s/4, columns c0 + 4(s%4); the lane i of the group receives
+// column c0 + i of rows r0..r0+3.  r0 must be a multiple of 4, c0 of 16.
+template <int D>
+__device__ inline bf16x4 lds_tr4(const char* base, int r0, int c0, int s) {
+  const int r = r0 + (s >> 2);
+  const int col = c0 + 4 * (s & 3);
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(base + Swz<D>::off(r, col)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ inline bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+}  // namespace cp
