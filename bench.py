@@ -139,8 +139,10 @@ class Workload:
 
 
 def kernel_times(wl, cp, torch, iters):
-    """Average duration (ms) of the forward and backward chunk kernels alone,
-    HIP events on the stream they are launched on."""
+    """Average duration (ms) of each hot kernel launched alone, timed with HIP
+    events on the stream it is launched on: the forward chunk kernel, the two
+    backward kernels (dK/dV and dQ) and the LSE merge.  Returns a dict with the
+    algorithmic work of one launch of each."""
     st = torch.cuda.current_stream()
     if wl.name in ("ring_128k", "usp_1m"):
         S, P = wl.S, wl.P
@@ -150,8 +152,7 @@ def kernel_times(wl, cp, torch, iters):
         ks = cp.make_span(0, c, (2 * P - 1) * c, c)           # step 0: the rank's own KV
         k, v = wl.k[:n], wl.v[:n]
         pairs = 2 * c * c + c
-        dk = wl.dk[:n]
-        dv = wl.dv[:n]
+        dk, dv = wl.dk[:n], wl.dv[:n]
     else:
         qs = cp.make_span(0, wl.rows, 0, 0, wl.doc)
         ks = cp.make_span(0, wl.rows, 0, 0, wl.doc)
@@ -159,21 +160,35 @@ def kernel_times(wl, cp, torch, iters):
         pairs = wl.pairs_per_head
         dk, dv = wl.dk, wl.dv
     o32 = torch.empty(wl.rows, wl.hq, wl.d, device=wl.dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    lse2 = torch.empty_like(wl.lse)
+    o_part = torch.empty_like(o32)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     cp.cp_attn_chunk_fwd(wl.sh, wl.q, qs, k, v, ks, wl.o, wl.lse)
     cp.cp_attn_delta(wl.o, wl.dout, wl.delta)
+    cp.cp_attn_chunk_fwd(wl.sh, wl.q, qs, k, v, ks, o_part, lse2)
     torch.cuda.synchronize()
     ev[0].record(st)
     for _ in range(iters):
-        cp.cp_attn_chunk_fwd(wl.sh, wl.q, qs, k, v, ks, o32, wl.lse)
+        cp.cp_attn_chunk_fwd(wl.sh, wl.q, qs, k, v, ks, o32, lse2)
     ev[1].record(st)
     for _ in range(iters):
-        cp.cp_attn_chunk_bwd(wl.sh, wl.q, qs, k, v, ks, wl.dout, wl.lse, wl.delta, wl.dq, dk, dv)
+        cp.cp_attn_chunk_bwd_dkdv(wl.sh, wl.q, qs, k, v, ks, wl.dout, wl.lse, wl.delta, dk, dv)
     ev[2].record(st)
+    for _ in range(iters):
+        cp.cp_attn_chunk_bwd_dq(wl.sh, wl.q, qs, k, v, ks, wl.dout, wl.lse, wl.delta, wl.dq)
+    ev[3].record(st)
+    for _ in range(iters):      # merge a partial into an accumulator of the output's shape
+        cp.cp_lse_merge(o32, lse2, o_part, wl.lse)
+    ev[4].record(st)
     torch.cuda.synchronize()
-    t_fwd = ev[0].elapsed_time(ev[1]) / iters
-    t_bwd = ev[1].elapsed_time(ev[2]) / iters
-    return t_fwd, t_bwd, 4 * wl.d * pairs * wl.hq, 10 * wl.d * pairs * wl.hq
+    ms = [ev[i].elapsed_time(ev[i + 1]) / iters for i in range(4)]
+    rh = wl.rows * wl.hq
+    return {
+        "fwd_bf16_kernel": {"ms": ms[0], "flops": 4 * wl.d * pairs * wl.hq},
+        "dkdv_bf16_kernel": {"ms": ms[1], "flops": 8 * wl.d * pairs * wl.hq},
+        "dq_bf16_kernel": {"ms": ms[2], "flops": 6 * wl.d * pairs * wl.hq},
+        "merge_kernel": {"ms": ms[3], "bytes": rh * (3 * wl.d * 4 + 3 * 4)},
+    }
 
 
 def sampled_parity(wl, torch):
@@ -279,15 +294,22 @@ def main():
     if parity:
         out["parity_sample"] = parity
     if not args.no_kernel_timing:
-        t_fwd, t_bwd, f_fwd, f_bwd = kernel_times(wl, cp, torch, max(3, args.steps))
-        fw = f_fwd / (t_fwd * 1e-3) / 1e12
-        bw = f_bwd / (t_bwd * 1e-3) / 1e12
-        dom = ("bwd_bf16_kernel", bw, t_bwd) if t_bwd >= t_fwd else ("fwd_bf16_kernel", fw, t_fwd)
-        out["kernels"] = {"fwd_ms": round(t_fwd, 4), "fwd_tflops": round(fw, 1),
-                          "bwd_ms": round(t_bwd, 4), "bwd_tflops": round(bw, 1)}
-        out["roofline"] = {"kernel": dom[0], "bound": "mfma", "achieved": round(dom[1], 1),
+        kt = kernel_times(wl, cp, torch, max(3, args.steps))
+        out["kernels"] = {}
+        for name, r in kt.items():
+            e = {"ms": round(r["ms"], 4)}
+            if "flops" in r:
+                e["tflops"] = round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 1)
+            else:
+                e["gb_s"] = round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1)
+                e["frac_hbm_8tbs"] = round(r["bytes"] / (r["ms"] * 1e-3) / 8e12, 3)
+            out["kernels"][name] = e
+        dom = max((n for n in kt if "flops" in kt[n]), key=lambda n: kt[n]["ms"])
+        ach = kt[dom]["flops"] / (kt[dom]["ms"] * 1e-3) / 1e12
+        out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(dom[1] / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                           "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                           "flops_per_launch": kt[dom]["flops"], "ms_per_launch": round(kt[dom]["ms"], 4)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

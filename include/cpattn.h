@@ -138,6 +138,18 @@ cp_status cp_attn_chunk_bwd(const cp_shape *sh, const void *q, cp_span qs,
                             const float *lse, const float *delta,
                             float *dq, float *dk, float *dv, void *stream);
 
+/* The two halves of cp_attn_chunk_bwd, same arguments and layouts: the
+ * key-side gradients (dk, dv +=) and the query-side gradient (dq +=).  In a
+ * ring the visiting chunk's dk/dv travel back to its owner, so computing them
+ * first lets that transfer overlap the dq work. */
+cp_status cp_attn_chunk_bwd_dkdv(const cp_shape *sh, const void *q, cp_span qs,
+                                 const void *k, const void *v, cp_span ks, const void *dout,
+                                 const float *lse, const float *delta,
+                                 float *dk, float *dv, void *stream);
+cp_status cp_attn_chunk_bwd_dq(const cp_shape *sh, const void *q, cp_span qs,
+                               const void *k, const void *v, cp_span ks, const void *dout,
+                               const float *lse, const float *delta, float *dq, void *stream);
+
 /* Zigzag sharding for causal load balance ([MaxText] "헤드를 나누거나, KV를
  * 돌리거나" and [Llama3] "긴 문맥은...": later tokens see more context, so work
  * is balanced across ranks).  S tokens are cut into 2P chunks of c = S/(2P);

@@ -22,6 +22,7 @@ CP_BF16, CP_F32 = 0, 1
 
 EXPORTED = (
     "cp_attn_chunk_fwd", "cp_lse_merge", "cp_attn_delta", "cp_attn_chunk_bwd",
+    "cp_attn_chunk_bwd_dkdv", "cp_attn_chunk_bwd_dq",
     "cp_zigzag_layout", "cp_ring_schedule", "cp_ring_workspace_bytes", "cp_ring_emulate",
     "cp_ulysses_workspace_bytes", "cp_ulysses_share", "cp_tile_map", "cp_last_error",
     "cp_abi_version",
@@ -63,6 +64,8 @@ def load(path: str = LIB_PATH):
         "cp_lse_merge": (I32, [I64, I32, I32, P, P, P, P, P]),
         "cp_attn_delta": (I32, [I64, I32, I32, P, I32, P, I32, P, P]),
         "cp_attn_chunk_bwd": (I32, [SH, P, cp_span, P, P, cp_span, P, P, P, P, P, P, P]),
+        "cp_attn_chunk_bwd_dkdv": (I32, [SH, P, cp_span, P, P, cp_span, P, P, P, P, P, P]),
+        "cp_attn_chunk_bwd_dq": (I32, [SH, P, cp_span, P, P, cp_span, P, P, P, P, P]),
         "cp_zigzag_layout": (I32, [I64, I32, I32, ctypes.POINTER(ctypes.c_int64),
                                    ctypes.POINTER(ctypes.c_int32)]),
         "cp_ring_schedule": (I32, [I64, I32, I32, I32, ctypes.POINTER(ctypes.c_int32),
@@ -158,6 +161,19 @@ def cp_attn_chunk_bwd(shape, q, qs, k, v, ks, dout, lse, delta, dq, dk, dv, stre
     _check(lib.cp_attn_chunk_bwd(ctypes.byref(shape), _ptr(q), qs, _ptr(k), _ptr(v), ks,
                                  _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk),
                                  _ptr(dv), _stream(stream)))
+
+
+def cp_attn_chunk_bwd_dkdv(shape, q, qs, k, v, ks, dout, lse, delta, dk, dv, stream=None):
+    lib = load()
+    _check(lib.cp_attn_chunk_bwd_dkdv(ctypes.byref(shape), _ptr(q), qs, _ptr(k), _ptr(v), ks,
+                                      _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
+                                      _stream(stream)))
+
+
+def cp_attn_chunk_bwd_dq(shape, q, qs, k, v, ks, dout, lse, delta, dq, stream=None):
+    lib = load()
+    _check(lib.cp_attn_chunk_bwd_dq(ctypes.byref(shape), _ptr(q), qs, _ptr(k), _ptr(v), ks,
+                                    _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _stream(stream)))
 
 
 def cp_zigzag_layout(S, P, rank):

@@ -129,10 +129,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hh = lane >> 5;
 
-  const int32_t w = xcd_remap(blockIdx.x, gridDim.x);
-  if (w >= a.n_work) return;
-  const int kvh = w / a.nkt;
-  const int32_t kt = w % a.nkt;                        // ascending = heavy first
+  int32_t kvh, kt;                                      // ascending kt = heavy first
+  if (!xcd_work(blockIdx.x, a.hkv, a.nkt, kvh, kt)) return;
 
   const SpanD qs = a.qs, ks = a.ks;
   const int32_t Lq = span_len(qs), Lk = span_len(ks);
@@ -315,10 +313,9 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hh = lane >> 5;
 
-  const int32_t w = xcd_remap(blockIdx.x, gridDim.x);
-  if (w >= a.n_work) return;
-  const int32_t grp = w / a.nqt;
-  const int32_t qt = a.nqt - 1 - (w % a.nqt);          // heavy first
+  int32_t grp, hidx;
+  if (!xcd_work(blockIdx.x, a.hq / a.heads_per_wg, a.nqt, grp, hidx)) return;
+  const int32_t qt = a.nqt - 1 - hidx;                 // heavy first
   const int hpw = a.heads_per_wg;
   const int groups_per_kv = a.G / hpw;
   const int kvh = grp / groups_per_kv;
@@ -424,27 +421,34 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+hipError_t launch_bwd_bf16_dkdv(const BwdParams& p, hipStream_t stream) {
   if (span_len(p.qs) == 0 || span_len(p.ks) == 0) return hipSuccess;
   BwdParams a = p;
-  const int32_t Lk = span_len(a.ks), Lq = span_len(a.qs);
-  a.nkt = (Lk + BKG - 1) / BKG;
+  a.nkt = (span_len(a.ks) + BKG - 1) / BKG;
   a.n_work = a.nkt * a.hkv;
-  int32_t grid = round_up8(a.n_work);
+  const int32_t grid = xcd_grid(a.hkv, a.nkt);
   if (a.d == 128) hipLaunchKernelGGL(dkdv_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
   else hipLaunchKernelGGL(dkdv_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
 
+hipError_t launch_bwd_bf16_dq(const BwdParams& p, hipStream_t stream) {
+  if (span_len(p.qs) == 0 || span_len(p.ks) == 0) return hipSuccess;
   BwdParams b = p;
   b.heads_per_wg = b.G >= 4 ? 4 : b.G;
   b.qblocks_per_wg = 4 / b.heads_per_wg;
-  b.nqt = (Lq + BQ * b.qblocks_per_wg - 1) / (BQ * b.qblocks_per_wg);
+  b.nqt = (span_len(b.qs) + BQ * b.qblocks_per_wg - 1) / (BQ * b.qblocks_per_wg);
   b.n_work = b.nqt * (b.hq / b.heads_per_wg);
-  grid = round_up8(b.n_work);
+  const int32_t grid = xcd_grid(b.hq / b.heads_per_wg, b.nqt);
   if (b.d == 128) hipLaunchKernelGGL(dq_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, b);
   else hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, b);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+  hipError_t e = launch_bwd_bf16_dkdv(p, stream);
+  if (e != hipSuccess) return e;
+  return launch_bwd_bf16_dq(p, stream);
 }
 
 }  // namespace cp

@@ -250,18 +250,28 @@ hipError_t launch_fwd_f32(const FwdParams& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_f32(const BwdParams& a, hipStream_t stream) {
+hipError_t launch_bwd_f32_dq(const BwdParams& a, hipStream_t stream) {
   const int64_t qitems = (int64_t)span_len(a.qs) * a.hq;
-  const int64_t kitems = (int64_t)span_len(a.ks) * a.hkv;
-  if (qitems == 0 || kitems == 0) return hipSuccess;
-  if (a.d == 128) {
-    hipLaunchKernelGGL(dq_f32_kernel<128>, dim3((unsigned)((qitems + 3) / 4)), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(dkv_f32_kernel<128>, dim3((unsigned)((kitems + 3) / 4)), dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(dq_f32_kernel<64>, dim3((unsigned)((qitems + 3) / 4)), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(dkv_f32_kernel<64>, dim3((unsigned)((kitems + 3) / 4)), dim3(256), 0, stream, a);
-  }
+  if (qitems == 0 || span_len(a.ks) == 0) return hipSuccess;
+  const dim3 grid((unsigned)((qitems + 3) / 4));
+  if (a.d == 128) hipLaunchKernelGGL(dq_f32_kernel<128>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(dq_f32_kernel<64>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_f32_dkdv(const BwdParams& a, hipStream_t stream) {
+  const int64_t kitems = (int64_t)span_len(a.ks) * a.hkv;
+  if (kitems == 0 || span_len(a.qs) == 0) return hipSuccess;
+  const dim3 grid((unsigned)((kitems + 3) / 4));
+  if (a.d == 128) hipLaunchKernelGGL(dkv_f32_kernel<128>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(dkv_f32_kernel<64>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_f32(const BwdParams& a, hipStream_t stream) {
+  hipError_t e = launch_bwd_f32_dq(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_bwd_f32_dkdv(a, stream);
 }
 
 }  // namespace cp

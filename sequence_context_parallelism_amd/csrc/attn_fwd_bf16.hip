@@ -166,10 +166,9 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hh = lane >> 5;
 
-  const int32_t w = xcd_remap(blockIdx.x, gridDim.x);
-  if (w >= a.n_work) return;
-  const int32_t grp = w / a.nqt;
-  const int32_t qt = a.nqt - 1 - (w % a.nqt);         // heavy first
+  int32_t grp, hidx;
+  if (!xcd_work(blockIdx.x, a.hq / a.heads_per_wg, a.nqt, grp, hidx)) return;
+  const int32_t qt = a.nqt - 1 - hidx;                 // heavy first
   const int hpw = a.heads_per_wg;
   const int groups_per_kv = a.G / hpw;
   const int kvh = grp / groups_per_kv;
@@ -299,7 +298,7 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   const int32_t ngroups = a.hq / a.heads_per_wg;
   a.n_work = a.nqt * ngroups;
   if (a.n_work == 0) return hipSuccess;
-  const int32_t grid = round_up8(a.n_work);
+  const int32_t grid = xcd_grid(ngroups, a.nqt);
   if (a.d == 128) {
     hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
   } else {

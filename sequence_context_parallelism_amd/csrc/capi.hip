@@ -97,9 +97,11 @@ hipError_t run_fwd(const cp_shape* sh, const void* q, const cp_span& qs, const v
   return sh->dtype == CP_F32 ? launch_fwd_f32(p, st) : launch_fwd_bf16(p, st);
 }
 
+enum BwdPart { BWD_ALL, BWD_DKDV, BWD_DQ };
+
 hipError_t run_bwd(const cp_shape* sh, const void* q, const cp_span& qs, const void* k, const void* v,
                    const cp_span& ks, const void* dout, const float* lse, const float* delta,
-                   int64_t lse_ld, float* dq, float* dk, float* dv, hipStream_t st) {
+                   int64_t lse_ld, float* dq, float* dk, float* dv, hipStream_t st, BwdPart part = BWD_ALL) {
   BwdParams p{};
   p.q = (const __bf16*)q; p.k = (const __bf16*)k; p.v = (const __bf16*)v; p.dout = (const __bf16*)dout;
   p.qf = (const float*)q; p.kf = (const float*)k; p.vf = (const float*)v; p.doutf = (const float*)dout;
@@ -109,7 +111,12 @@ hipError_t run_bwd(const cp_shape* sh, const void* q, const cp_span& qs, const v
   p.scale = sh->scale; p.causal = sh->causal;
   p.lse = lse; p.delta = delta; p.lse_ld = lse_ld;
   p.dq = dq; p.dk = dk; p.dv = dv;
-  return sh->dtype == CP_F32 ? launch_bwd_f32(p, st) : launch_bwd_bf16(p, st);
+  const bool f32 = sh->dtype == CP_F32;
+  switch (part) {
+    case BWD_DKDV: return f32 ? launch_bwd_f32_dkdv(p, st) : launch_bwd_bf16_dkdv(p, st);
+    case BWD_DQ: return f32 ? launch_bwd_f32_dq(p, st) : launch_bwd_bf16_dq(p, st);
+    default: return f32 ? launch_bwd_f32(p, st) : launch_bwd_bf16(p, st);
+  }
 }
 
 #define CP_TRY_HIP(expr, what)                 \
@@ -214,9 +221,9 @@ cp_status cp_attn_delta(int64_t rows, int32_t h, int32_t d, const void* o, cp_dt
   return ok();
 }
 
-cp_status cp_attn_chunk_bwd(const cp_shape* sh, const void* q, cp_span qs, const void* k, const void* v,
-                            cp_span ks, const void* dout, const float* lse, const float* delta, float* dq,
-                            float* dk, float* dv, void* stream) {
+static cp_status chunk_bwd(const cp_shape* sh, const void* q, cp_span qs, const void* k, const void* v,
+                           cp_span ks, const void* dout, const float* lse, const float* delta, float* dq,
+                           float* dk, float* dv, void* stream, BwdPart part, const char* name) {
   CP_TRY(check_shape(sh));
   CP_TRY(check_span(qs, "qs"));
   CP_TRY(check_span(ks, "ks"));
@@ -227,13 +234,34 @@ cp_status cp_attn_chunk_bwd(const cp_shape* sh, const void* q, cp_span qs, const
   CP_TRY(check_ptr(k, "k"));
   CP_TRY(check_ptr(v, "v"));
   CP_TRY(check_ptr(dout, "dout"));
-  CP_TRY(check_ptr(dq, "dq"));
-  CP_TRY(check_ptr(dk, "dk"));
-  CP_TRY(check_ptr(dv, "dv"));
+  if (part != BWD_DKDV) CP_TRY(check_ptr(dq, "dq"));
+  if (part != BWD_DQ) {
+    CP_TRY(check_ptr(dk, "dk"));
+    CP_TRY(check_ptr(dv, "dv"));
+  }
   if (!lse || !delta) return fail(CP_ERR_ARG, "lse or delta is NULL");
-  CP_TRY_HIP(run_bwd(sh, q, qs, k, v, ks, dout, lse, delta, Lq, dq, dk, dv, (hipStream_t)stream),
-             "cp_attn_chunk_bwd");
+  CP_TRY_HIP(run_bwd(sh, q, qs, k, v, ks, dout, lse, delta, Lq, dq, dk, dv, (hipStream_t)stream, part), name);
   return ok();
+}
+
+cp_status cp_attn_chunk_bwd(const cp_shape* sh, const void* q, cp_span qs, const void* k, const void* v,
+                            cp_span ks, const void* dout, const float* lse, const float* delta, float* dq,
+                            float* dk, float* dv, void* stream) {
+  return chunk_bwd(sh, q, qs, k, v, ks, dout, lse, delta, dq, dk, dv, stream, BWD_ALL, "cp_attn_chunk_bwd");
+}
+
+cp_status cp_attn_chunk_bwd_dkdv(const cp_shape* sh, const void* q, cp_span qs, const void* k, const void* v,
+                                 cp_span ks, const void* dout, const float* lse, const float* delta, float* dk,
+                                 float* dv, void* stream) {
+  return chunk_bwd(sh, q, qs, k, v, ks, dout, lse, delta, nullptr, dk, dv, stream, BWD_DKDV,
+                   "cp_attn_chunk_bwd_dkdv");
+}
+
+cp_status cp_attn_chunk_bwd_dq(const cp_shape* sh, const void* q, cp_span qs, const void* k, const void* v,
+                               cp_span ks, const void* dout, const float* lse, const float* delta, float* dq,
+                               void* stream) {
+  return chunk_bwd(sh, q, qs, k, v, ks, dout, lse, delta, dq, nullptr, nullptr, stream, BWD_DQ,
+                   "cp_attn_chunk_bwd_dq");
 }
 
 cp_status cp_zigzag_layout(int64_t S, int32_t P, int32_t rank, int64_t pos0[2], int32_t len[2]) {

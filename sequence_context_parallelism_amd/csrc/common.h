@@ -110,12 +110,42 @@ __device__ inline int32_t wave_lower_bound(const int32_t* doc, int32_t n, int32_
   return r < hi ? r : hi;
 }
 
-// XCD-aware remap: work-groups are dispatched round-robin over the 8 XCDs, so
-// blockIdx b runs on XCD b % 8.  Give each XCD a contiguous range of logical
-// work ids so that work sharing K/V data shares that XCD's L2.  The grid size
-// must be a multiple of 8.
-__device__ inline int32_t xcd_remap(int32_t b, int32_t nb) {
-  return (b & 7) * (nb >> 3) + (b >> 3);
+// XCD-aware, load-balanced work order.  Work-groups are dispatched in
+// blockIdx order, round-robin over the 8 XCDs (blockIdx b runs on XCD b % 8).
+// A kernel's work is `ngroups` independent groups (the items of a group share
+// one KV head, hence that XCD's L2) of `nidx` items each, item 0 the heaviest.
+// The map gives every XCD the same mix of heavy and light items and keeps a
+// group's items on as few XCDs as possible:
+//   * 8 % ngroups == 0: group = xcd % ngroups, and the 8/ngroups XCDs of a
+//     group take its items round-robin, heaviest first;
+//   * ngroups % 8 == 0: XCD x takes groups x, x+8, ..., heaviest items first;
+//   * otherwise: items in heaviest-first order, groups interleaved.
+// Returns false for a padding block (no item).
+__device__ inline bool xcd_work(int32_t b, int32_t ngroups, int32_t nidx, int32_t& group, int32_t& idx) {
+  const int32_t xcd = b & 7, slot = b >> 3;
+  if ((8 % ngroups) == 0) {
+    const int32_t per = 8 / ngroups;
+    group = xcd % ngroups;
+    idx = slot * per + xcd / ngroups;
+    return idx < nidx;
+  }
+  if ((ngroups % 8) == 0) {
+    const int32_t m = ngroups / 8;
+    group = xcd + 8 * (slot % m);
+    idx = slot / m;
+    return idx < nidx;
+  }
+  group = b % ngroups;
+  idx = b / ngroups;
+  return idx < nidx;
+}
+
+__host__ inline int32_t xcd_grid(int32_t ngroups, int32_t nidx) {
+  int64_t n;
+  if ((8 % ngroups) == 0) n = 8 * (((int64_t)nidx + 8 / ngroups - 1) / (8 / ngroups));
+  else if ((ngroups % 8) == 0) n = (int64_t)ngroups * nidx;
+  else n = (((int64_t)ngroups * nidx + 7) / 8) * 8;
+  return (int32_t)n;
 }
 
 __host__ inline int32_t round_up8(int32_t n) { return (n + 7) & ~7; }

@@ -55,9 +55,13 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);       // dkdv then dq
+hipError_t launch_bwd_bf16_dkdv(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_bf16_dq(const BwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
-hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t stream);        // dq then dkdv
+hipError_t launch_bwd_f32_dkdv(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_f32_dq(const BwdParams& p, hipStream_t stream);
 
 // acc <- acc (+) part, exact LSE-weighted combination; rows x h row-heads
 hipError_t launch_lse_merge(int64_t rows, int h, int d, float* o_acc, float* lse_acc, int64_t acc_ld,

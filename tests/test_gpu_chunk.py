@@ -20,6 +20,8 @@ CASES = [
     ("docs_g8", 8, 1, 128, (0, 300), (0, 300), True, True),
     ("offset_rows_empty", 4, 2, 64, (10, 50), (40, 130), True, False),
     ("docs_two_runs_d64", 4, 2, 64, (0, 64, 192, 64), (0, 128, 128, 128), True, True),
+    ("three_kv_heads", 12, 3, 64, (0, 150), (0, 150), True, False),     # groups not dividing 8
+    ("sixteen_kv_heads", 64, 16, 64, (0, 70), (0, 70), True, False),    # groups a multiple of 8
 ]
 
 
@@ -197,3 +199,32 @@ def test_mask_probe_recovers_mask_exactly(gpu_lib, dtype):
         live = cnt > 0
         assert np.array_equal(np.rint(np.exp(ln[h, live])).astype(int), cnt[live])
         assert np.all(np.isneginf(ln[h, ~live]))
+
+
+def test_backward_deterministic_and_split_equals_combined(gpu_lib):
+    """The backward uses no atomics: two runs are bitwise identical, and the
+    dK/dV and dQ halves called separately give the same bits as the whole."""
+    c = _setup(CASES[0], torch.bfloat16, seed=4)
+    Lq, Lk = len(c["qpos"]), len(c["kpos"])
+    o, lse = _gpu_fwd(c, torch.bfloat16)
+    delta = torch.empty(c["hq"], Lq, device=DEV)
+    cp.cp_attn_delta(o, c["dod"], delta)
+    outs = []
+    for _ in range(2):
+        dq = torch.zeros(Lq, c["hq"], c["d"], device=DEV)
+        dk = torch.zeros(Lk, c["hkv"], c["d"], device=DEV)
+        dv = torch.zeros_like(dk)
+        cp.cp_attn_chunk_bwd(c["sh"], c["qd"], c["qs"], c["kd"], c["vd"], c["ks"], c["dod"], lse, delta,
+                             dq, dk, dv)
+        outs.append((dq, dk, dv))
+    dq = torch.zeros(Lq, c["hq"], c["d"], device=DEV)
+    dk = torch.zeros(Lk, c["hkv"], c["d"], device=DEV)
+    dv = torch.zeros_like(dk)
+    cp.cp_attn_chunk_bwd_dkdv(c["sh"], c["qd"], c["qs"], c["kd"], c["vd"], c["ks"], c["dod"], lse, delta, dk, dv)
+    cp.cp_attn_chunk_bwd_dq(c["sh"], c["qd"], c["qs"], c["kd"], c["vd"], c["ks"], c["dod"], lse, delta, dq)
+    outs.append((dq, dk, dv))
+    torch.cuda.synchronize()
+    for x, y in zip(outs[0], outs[1]):
+        assert torch.equal(x, y)
+    for x, y in zip(outs[0], outs[2]):
+        assert torch.equal(x, y)
