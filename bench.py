@@ -44,6 +44,9 @@ def parse():
                     choices=["ulysses_64k", "ring_128k", "docs_128k", "usp_1m"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (3 times), the reference for "
+                         "scaling HBM traffic counters")
     return ap.parse_args()
 
 
@@ -257,6 +260,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     cp.load()
+    if args.copy_calibration:
+        n = 512 * 2**20 // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}), flush=True)
+        return
     wl = Workload(args.workload, torch, cp, cpinputs)
     torch.cuda.synchronize()
     print(f"[bench] workload {args.workload} ready", file=sys.stderr, flush=True)

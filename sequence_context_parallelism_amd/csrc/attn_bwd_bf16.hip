@@ -74,30 +74,42 @@ __device__ inline void dkdv_tile(KvState<D>& st, const char* Qt, const char* Ot,
     }
   }
   // accumulator element r of block qb: key = lane's key, query row qb*32 + 8(r/4) + 4hh + r%4
-  bf16x8 pf[4], dsf[4];
+  float p[2][16];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int qr0 = qb * 32 + j * 8 + hh * 4;
-      const f32x4 l4 = *(const f32x4*)(Lt + qr0);
-      const f32x4 d4 = *(const f32x4*)(Dlt + qr0);
+      const f32x4 l4 = *(const f32x4*)(Lt + qb * 32 + j * 8 + hh * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[qb][j * 4 + i] = __builtin_amdgcn_exp2f(fmaf(s[qb][j * 4 + i], c, -l4[i] * LOG2E));
+    }
+  if (mask) {
+    asm volatile("; partial tile" ::: "memory");   // a real branch, not predicated code
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = qb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+        const int32_t qidx = qa0 + qr;
+        const bool ok = st.kvalid & (qidx < Lq) & (qidx >= st.qlim) & (!docs | (QDt[qr] == st.kdoc));
+        p[qb][r] = ok ? p[qb][r] : 0.f;
+      }
+  }
+  bf16x8 pf[4], dsf[4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 d4 = *(const f32x4*)(Dlt + qb * 32 + j * 8 + hh * 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = j * 4 + i;
-        float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -l4[i] * LOG2E));
-        if (mask) {
-          const int32_t qidx = qa0 + qr0 + i;
-          const bool ok = st.kvalid & (qidx < Lq) & (qidx >= st.qlim) & (!docs | (QDt[qr0 + i] == st.kdoc));
-          p = ok ? p : 0.f;
-        }
-        const float ds = p * (dp[qb][r] - d4[i]) * scale;
+        const float ds = p[qb][r] * (dp[qb][r] - d4[i]) * scale;
         const int t = qb * 2 + (r >> 3), sl = r & 7;
-        pf[t][sl] = (__bf16)p;
+        pf[t][sl] = (__bf16)p[qb][r];
         dsf[t][sl] = (__bf16)ds;
       }
     }
-  }
   // dV^T += dO^T P, dK^T += Q^T dS: A operands = transposed reads of the tiles
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -206,6 +218,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
       live = live && kd_hi >= qd_lo && kd_lo <= qd_hi;
       full = full && qd_lo == qd_hi && kd_lo == kd_hi && kd_lo == qd_lo;
     }
+    live = __builtin_amdgcn_readfirstlane((int)live) != 0;   // wave-uniform: scalar branches
+    full = __builtin_amdgcn_readfirstlane((int)full) != 0;
     if (live) dkdv_tile<D>(st, Qc, Oc, Lc, Dc, Xc, qa0, Lq, !full, docs, c, a.scale, lane);
     wait_vm0();
     __syncthreads();
@@ -269,21 +283,29 @@ __device__ inline void dq_tile(QState<D>& st, const char* Kt, const char* Vt, co
       }
     }
     // element r of block qb: query = lane's column of block qb, key = kb*32 + 8(r/4) + 4hh + r%4
-    bf16x8 dsf[2][2];
+    float p[2][16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kk = kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-      const int32_t kd_ = Dt[kk];
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, st.nl[qb]));
-        if (mask) {
+      for (int r = 0; r < 16; ++r) p[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, st.nl[qb]));
+    if (mask) {
+      asm volatile("; partial tile" ::: "memory");   // a real branch, not predicated code
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+        const int32_t kd_ = Dt[kk];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
           const bool ok = (kb0 + kk < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
-          p = ok ? p : 0.f;
+          p[qb][r] = ok ? p[qb][r] : 0.f;
         }
-        dsf[qb][r >> 3][r & 7] = (__bf16)(p * (dp[qb][r] - st.dl[qb]) * scale);
       }
     }
+    bf16x8 dsf[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dsf[qb][r >> 3][r & 7] = (__bf16)(p[qb][r] * (dp[qb][r] - st.dl[qb]) * scale);
     // dQ^T[qb][db] += K^T (d rows, 16 keys per step) x dS^T
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -390,6 +412,8 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
       live = live && kd_hi >= qd_lo && kd_lo <= qd_hi;
       full = full && qd_lo == qd_hi && kd_lo == kd_hi && kd_lo == qd_lo;
     }
+    live = __builtin_amdgcn_readfirstlane((int)live) != 0;   // wave-uniform: scalar branches
+    full = __builtin_amdgcn_readfirstlane((int)full) != 0;
     if (live) dq_tile<D>(st, Kc, Vc, Xc, kb0, !full, docs, c, a.scale, lane);
     wait_vm0();
     __syncthreads();

@@ -18,17 +18,22 @@
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the K tile is the A operand
 //     (ds_read_b128), the wave's Q rows are the B operand (in VGPRs for the
 //     whole kernel).  Each lane holds one query column and 16 key rows of the
-//     32x32 accumulator, so a row's statistics need one cross-lane exchange.
+//     32x32 accumulator.
 //   * O^T += V^T P^T: P^T goes from the S^T accumulator straight into the B
 //     operand; V^T is read with the LDS transpose read ds_read_b64_tr_b16.
-//   * softmax in base 2 with the scale folded into one FMA; the running max
-//     is raised only when a tile's max exceeds it by more than 2^8 (the
-//     accumulators are then rescaled), which is exact and makes rescaling
-//     rare.
+//   * Softmax reference point.  Each row's exponent offset m is fixed at the
+//     max of the first tile in which the row has an allowed key, and never
+//     moves: P = exp2((s - m) c) may exceed 1 for later keys, and the result
+//     O = sum P v / sum P, LSE = m + ln sum P is the same.  No running max, no
+//     rescaling of the accumulators, no per-tile max in the common path.  A
+//     tile whose row sum exceeds 2^64 (a score more than ~44 above m, in
+//     natural-log units) flags the work-group, which then redoes its rows
+//     with the exact online softmax (running max, rescale), so any input is
+//     handled; for ordinary inputs the flag never fires.
 //   * fully masked tiles (causal or document) are skipped; the element mask is
 //     evaluated only on partial tiles and on the ragged last tile.
 //   * work-groups run heavy-first (later query tiles have more causal work),
-//     remapped so each XCD works on a contiguous range of KV heads.
+//     spread so that every XCD gets the same mix (common.h, xcd_work).
 #include "common.h"
 #include "kernels.h"
 #include "tile_io.h"
@@ -44,7 +49,7 @@ constexpr int BK = 64;      // keys per tile
 constexpr int QW = 64;      // query rows per wave
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-constexpr float RESCALE_LOG2 = 8.0f;   // lazy rescale threshold (base-2 units)
+constexpr float ROWSUM_LIMIT = 18446744073709551616.0f;   // 2^64
 
 __device__ inline void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -52,105 +57,126 @@ template <int D>
 struct FwdState {
   bf16x8 qf[2][D / 16];     // B operands: this wave's 64 query rows
   f32x16 oacc[2][D / 32];   // O^T accumulators [query block][d block]
-  float mrow[2];            // running max (raw score units), per query block
+  float moff[2];            // -m * c of the lane's query column (0 while unset)
+  float mrow[2];            // m (raw score units); -inf while unset
   float lrow[2];            // this lane's share of the row sum
   int32_t lim[2];           // keys [0, lim) are causally visible (and < Lk)
   int32_t qdoc[2];
 };
 
-// Element mask of a partial or ragged half-tile (32 keys from kh0).  Positions
-// increase along local order, so "key position <= query position" is
-// "key index < lim".
+// Scores of a 64-key tile: S^T[kb][qb] = K (keys kb*32..) Q^T (queries qb*32..)
 template <int D>
-__device__ inline void fwd_mask(const FwdState<D>& st, f32x16 (&s)[2], const int32_t* Dt, int32_t kb0,
-                                int kh0, bool docs, int hh) {
+__device__ inline void fwd_scores(const FwdState<D>& st, const char* Kt, f32x16 (&s)[2][2], int lane) {
+  const int lq = lane & 31, hh = lane >> 5;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int kk = kh0 + (r >> 2) * 8 + hh * 4 + (r & 3);
-    const int32_t kidx = kb0 + kk;
-    const int32_t kd_ = Dt[kk];
+  for (int kb = 0; kb < 2; ++kb) {
+    const bf16x8 ka = lds_row8<D>(Kt, kb * 32 + lq, hh * 8);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const bool ok = (kidx < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
-      s[qb][r] = ok ? s[qb][r] : -INFINITY;
+    for (int qb = 0; qb < 2; ++qb)
+      s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[qb][0], f32x16{}, 0, 0, 0);
+  }
+#pragma unroll
+  for (int kd = 1; kd < D / 16; ++kd) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 ka = lds_row8<D>(Kt, kb * 32 + lq, kd * 16 + hh * 8);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[qb][kd], s[kb][qb], 0, 0, 0);
     }
   }
 }
 
-// One 64-key tile for one wave, as two 32-key halves: scores, mask, online
-// softmax, O += P V.
+// Element mask of a partial or ragged tile.  Positions increase along local
+// order, so "key position <= query position" is "key index < lim".
 template <int D>
-__device__ inline void fwd_tile(FwdState<D>& st, const char* Kt, const char* Vt, const int32_t* Dt,
-                                int32_t kb0, bool mask, bool docs, float c, int lane) {
-  const int lq = lane & 31, hh = lane >> 5;
-  const int s16 = lane & 15, cg = (lane >> 4) & 1;
-  const float thr = RESCALE_LOG2 / c;
+__device__ inline void fwd_mask(const FwdState<D>& st, f32x16 (&s)[2][2], const int32_t* Dt, int32_t kb0,
+                                bool docs, int hh) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    // S^T[qb]: keys kb*32.. (rows) x queries qb*32.. (columns)
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kd = 0; kd < D / 16; ++kd) {
-      const bf16x8 ka = lds_row8<D>(Kt, kb * 32 + lq, kd * 16 + hh * 8);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[qb][kd], s[qb], 0, 0, 0);
-    }
-    if (mask) fwd_mask<D>(st, s, Dt, kb0, kb * 32, docs, hh);
-
-    float mx[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float m0 = fmaxf(s[qb][0], s[qb][1]);
-#pragma unroll
-      for (int r = 2; r < 16; r += 2) m0 = fmaxf(m0, fmaxf(s[qb][r], s[qb][r + 1]));
-      mx[qb] = fmaxf(m0, __shfl_xor(m0, 32));
-    }
-    // raise the running max only when the block exceeds it by > 2^8
-    const bool grow = (mx[0] > st.mrow[0] + thr) | (mx[1] > st.mrow[1] + thr);
-    if (__builtin_expect(__any(grow), 0)) {
+    for (int r = 0; r < 16; ++r) {
+      const int kk = kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+      const int32_t kidx = kb0 + kk;
+      const int32_t kd_ = Dt[kk];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const float mn = fmaxf(st.mrow[qb], mx[qb]);
-        const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((st.mrow[qb] - mn) * c);
-        st.lrow[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) st.oacc[qb][db] *= alpha;
-        st.mrow[qb] = mn;
+        const bool ok = (kidx < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
+        s[kb][qb][r] = ok ? s[kb][qb][r] : -INFINITY;
       }
     }
+}
+
+// Row max of a tile's scores per query column (both lane halves combined).
+__device__ inline void fwd_tile_max(const f32x16 (&s)[2][2], float (&mx)[2]) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float m0 = fmaxf(s[0][qb][0], s[0][qb][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) m0 = fmaxf(m0, fmaxf(s[0][qb][r], s[0][qb][r + 1]));
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) m0 = fmaxf(m0, fmaxf(s[1][qb][r], s[1][qb][r + 1]));
+    mx[qb] = fmaxf(m0, __shfl_xor(m0, 32));
+  }
+}
+
+// P = exp2(s c - m c), row sums, and O^T += V^T P^T.  Returns this lane's
+// largest tile row-sum share (for the overflow check).
+template <int D>
+__device__ inline float fwd_accumulate(FwdState<D>& st, const char* Vt, const f32x16 (&s)[2][2], float c,
+                                       int lane) {
+  const int hh = lane >> 5, s16 = lane & 15, cg = (lane >> 4) & 1;
+  float tsum[2] = {0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
     bf16x8 pf[2][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float moff = (st.mrow[qb] == -INFINITY) ? 0.f : -st.mrow[qb] * c;
-      float sum = 0.f;
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][t * 8 + i], c, moff));
-          sum += p;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][t * 8 + i], c, st.moff[qb]));
+          tsum[qb] += p;
           pf[qb][t][i] = (__bf16)p;
         }
-      }
-      st.lrow[qb] += sum;
-    }
-
-    // O^T[qb][db] += V^T (d rows db*32.., 16 keys per step) x P^T
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int k0 = kb * 32 + 16 * t;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int c0 = db * 32 + 16 * cg;
-        const bf16x8 va = cat8(lds_tr4<D>(Vt, k0 + 4 * hh, c0, s16),
-                               lds_tr4<D>(Vt, k0 + 8 + 4 * hh, c0, s16));
+        const bf16x8 va = cat8(lds_tr4<D>(Vt, k0 + 4 * hh, c0, s16), lds_tr4<D>(Vt, k0 + 8 + 4 * hh, c0, s16));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           st.oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][t], st.oacc[qb][db], 0, 0, 0);
       }
     }
   }
+  st.lrow[0] += tsum[0];
+  st.lrow[1] += tsum[1];
+  return fmaxf(tsum[0], tsum[1]);
+}
+
+// Exact online softmax for one tile (the fallback path): running max and
+// rescaling of the accumulators whenever the max rises.
+template <int D>
+__device__ inline void fwd_tile_exact(FwdState<D>& st, const char* Vt, f32x16 (&s)[2][2], float c, int lane) {
+  float mx[2];
+  fwd_tile_max(s, mx);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float mn = fmaxf(st.mrow[qb], mx[qb]);
+    if (mn > st.mrow[qb]) {
+      const float alpha = (st.mrow[qb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((st.mrow[qb] - mn) * c);
+      st.lrow[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) st.oacc[qb][db] *= alpha;
+      st.mrow[qb] = mn;
+      st.moff[qb] = -mn * c;
+    }
+  }
+  fwd_accumulate<D>(st, Vt, s, c, lane);
 }
 
 template <int D>
@@ -162,6 +188,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
   __shared__ __attribute__((aligned(16))) char vb1_[TB];
   __shared__ __attribute__((aligned(16))) int32_t db0_[BK];
   __shared__ __attribute__((aligned(16))) int32_t db1_[BK];
+  __shared__ int32_t overflow_flag;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hh = lane >> 5;
@@ -206,9 +233,20 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
     }
   };
   if (kt0 < kt1) issue(kt0, kb0_, vb0_, db0_);
+  if (tid == 0) overflow_flag = 0;
 
   // ---- this wave's Q rows as MFMA B operands ----------------------------
   FwdState<D> st;
+  auto reset = [&]() {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) st.oacc[qb][db] = f32x16{};
+      st.mrow[qb] = -INFINITY;
+      st.moff[qb] = 0.f;
+      st.lrow[qb] = 0.f;
+    }
+  };
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int32_t row = min(q0 + qb * 32 + lq, Lq - 1);
@@ -217,15 +255,9 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
     for (int kd = 0; kd < D / 16; ++kd) st.qf[qb][kd] = src[kd * 2];
     st.lim[qb] = causal ? min(Lk, span_count_le(ks, span_pos(qs, row))) : Lk;
     st.qdoc[qb] = docs ? qs.doc[row] : 0;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) st.oacc[qb][db] = f32x16{};
-    st.mrow[qb] = -INFINITY;
-    st.lrow[qb] = 0.f;
   }
+  reset();
   const float c = a.scale_log2;              // scale * log2(e)
-
-  wait_vm0();
-  __syncthreads();
 
   // wave-uniform bounds for classifying tiles: keys [0, lim_lo) are visible to
   // every row of the wave, keys >= lim_hi to none; doc ids of the first and
@@ -235,24 +267,88 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
   const int32_t qd_lo = docs ? qs.doc[q0 < Lq ? q0 : Lq - 1] : 0;
   const int32_t qd_hi = docs ? qs.doc[q1 - 1] : 0;
 
-  auto step = [&](int32_t kt, const char* Kc, const char* Vc, const int32_t* Dc, char* Kn, char* Vn,
-                  int32_t* Dn) {
-    if (kt + 1 < kt1) issue(kt + 1, Kn, Vn, Dn);
+  auto classify = [&](int32_t kt, const int32_t* Dc, bool& live, bool& full) {
     const int32_t kb0 = kt * BK, kb1 = min(Lk, kb0 + BK);
-    bool live = wave_live && kb0 < lim_hi;
-    bool full = kb1 - kb0 == BK && kb1 <= lim_lo;
+    live = wave_live && kb0 < lim_hi;
+    full = kb1 - kb0 == BK && kb1 <= lim_lo;
     if (docs) {
       const int32_t kd_lo = Dc[0], kd_hi = Dc[kb1 - kb0 - 1];
       live = live && kd_hi >= qd_lo && kd_lo <= qd_hi;
       full = full && qd_lo == qd_hi && kd_lo == kd_hi && kd_lo == qd_lo;
     }
-    if (live) fwd_tile<D>(st, Kc, Vc, Dc, kb0, !full, docs, c, lane);
+    // wave-uniform by construction; make it scalar so the branches are too
+    live = __builtin_amdgcn_readfirstlane((int)live) != 0;
+    full = __builtin_amdgcn_readfirstlane((int)full) != 0;
+  };
+
+  wait_vm0();
+  __syncthreads();
+
+  // ---- main loop: fixed reference point, accumulators touched by MFMA only --
+  float worst = 0.f;   // largest tile row-sum share seen by this lane
+  auto tile = [&](int32_t kt, const char* Kc, const char* Vc, const int32_t* Dc, char* Kn, char* Vn,
+                  int32_t* Dn) {
+    if (kt + 1 < kt1) issue(kt + 1, Kn, Vn, Dn);
+    bool live, full;
+    classify(kt, Dc, live, full);
+    if (live) {
+      f32x16 s[2][2];
+      fwd_scores<D>(st, Kc, s, lane);
+      if (!full) {
+        asm volatile("; partial tile" ::: "memory");   // a real branch, not predicated code
+        fwd_mask<D>(st, s, Dc, kt * BK, docs, hh);
+      }
+      if (__builtin_expect(__any((st.mrow[0] == -INFINITY) | (st.mrow[1] == -INFINITY)), 0)) {
+        // rows without a reference point yet take this tile's max (their
+        // accumulators are still zero, so nothing is rescaled)
+        asm volatile("; first tile" ::: "memory");
+        float mx[2];
+        fwd_tile_max(s, mx);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          if (st.mrow[qb] == -INFINITY && mx[qb] != -INFINITY) {
+            st.mrow[qb] = mx[qb];
+            st.moff[qb] = -mx[qb] * c;
+          }
+        }
+      }
+      worst = fmaxf(worst, fwd_accumulate<D>(st, Vc, s, c, lane));
+    }
     wait_vm0();
     __syncthreads();
   };
   for (int32_t kt = kt0; kt < kt1; kt += 2) {
-    step(kt, kb0_, vb0_, db0_, kb1_, vb1_, db1_);
-    if (kt + 1 < kt1) step(kt + 1, kb1_, vb1_, db1_, kb0_, vb0_, db0_);
+    tile(kt, kb0_, vb0_, db0_, kb1_, vb1_, db1_);
+    if (kt + 1 < kt1) tile(kt + 1, kb1_, vb1_, db1_, kb0_, vb0_, db0_);
+  }
+
+  // ---- fallback: a row sum grew past 2^64 -> redo with the exact algorithm --
+  if (__any(!(worst <= ROWSUM_LIMIT)) && lane == 0) atomicOr(&overflow_flag, 1);
+  __syncthreads();
+  if (overflow_flag != 0) {
+    asm volatile("; exact fallback" ::: "memory");
+    reset();
+    if (kt0 < kt1) issue(kt0, kb0_, vb0_, db0_);
+    wait_vm0();
+    __syncthreads();
+    auto tile_exact = [&](int32_t kt, const char* Kc, const char* Vc, const int32_t* Dc, char* Kn, char* Vn,
+                          int32_t* Dn) {
+      if (kt + 1 < kt1) issue(kt + 1, Kn, Vn, Dn);
+      bool live, full;
+      classify(kt, Dc, live, full);
+      if (live) {
+        f32x16 s[2][2];
+        fwd_scores<D>(st, Kc, s, lane);
+        if (!full) fwd_mask<D>(st, s, Dc, kt * BK, docs, hh);
+        fwd_tile_exact<D>(st, Vc, s, c, lane);
+      }
+      wait_vm0();
+      __syncthreads();
+    };
+    for (int32_t kt = kt0; kt < kt1; kt += 2) {
+      tile_exact(kt, kb0_, vb0_, db0_, kb1_, vb1_, db1_);
+      if (kt + 1 < kt1) tile_exact(kt + 1, kb1_, vb1_, db1_, kb0_, vb0_, db0_);
+    }
   }
 
   // ---- epilogue -----------------------------------------------------------

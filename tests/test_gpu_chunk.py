@@ -228,3 +228,28 @@ def test_backward_deterministic_and_split_equals_combined(gpu_lib):
         assert torch.equal(x, y)
     for x, y in zip(outs[0], outs[2]):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_forward_exact_fallback_on_growing_scores(gpu_lib, causal):
+    """Scores that rise by ~100 (natural-log units) along the keys: the first
+    tile's max is far below later scores, the row sums pass 2^64 and the
+    kernel must redo the rows with the exact online softmax."""
+    L, hq, hkv, d = 256, 4, 2, 128
+    rng = np.random.default_rng(17)
+    beta = np.linspace(0.0, 10.0, L).astype(np.float32)          # grows along the keys
+    qh = np.ones((L, hq, d), np.float32)
+    kh = np.repeat(beta[:, None, None], hkv, axis=1) * np.ones((1, 1, d), np.float32)
+    vh = rng.standard_normal((L, hkv, d)).astype(np.float32)
+    q, k, v = (to_dev(x, torch.bfloat16) for x in (qh, kh, vh))
+    qx, kx, vx = (t.to(torch.float64).cpu().numpy() for t in (q, k, v))   # exact bf16 values
+    pos = np.arange(L)
+    ro, rl = A.forward(qx, kx, vx, pos, pos, scale=1 / np.sqrt(d), causal=causal)
+    sh = shape_for(hq, hkv, d, torch.bfloat16, causal)
+    o = torch.empty(L, hq, d, device=DEV)
+    lse = torch.empty(hq, L, device=DEV)
+    cp.cp_attn_chunk_fwd(sh, q, cp.make_span(0, L), k, v, cp.make_span(0, L), o, lse)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(host(o)))
+    assert max_abs(host(o), ro) <= 2e-2
+    assert lse_err(host(lse), rl) <= 1e-3
