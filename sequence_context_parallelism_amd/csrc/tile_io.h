@@ -7,8 +7,14 @@
 // patterns the MFMA operands need are free of bank conflicts:
 //   * row reads: 16 lanes each read one 16-byte chunk of 16 consecutive rows
 //     (ds_read_b128, operand with the contraction along d);
-//   * transposed reads: ds_read_b64_tr_b16 over 4 consecutive rows x 16
-//     columns per 16-lane group (operand with the contraction along rows).
+//   * transposed reads: ds_read_b64_tr_b16, 32 lanes covering 4 consecutive
+//     rows (aligned to 4) x 4 consecutive chunks (operand with the
+//     contraction along rows).
+// For d = 128 a row is 256 bytes, one full sweep of the 64 LDS banks, so the
+// bank group (16 bytes) of chunk c of row r is its position c ^ f(r) with
+// f(r) = 4 (r mod 4) + (r / 4 mod 4): a permutation of 0..15 over any 16
+// aligned rows (row reads), and 4 (b ^ i) + (j ^ a) over rows 4a + i,
+// chunks 4b + j (transposed reads) -- 16 distinct groups in both cases.
 //
 // ds_read_b64_tr_b16 (measured on gfx950): within each 16-lane group, if
 // source lane s reads the 4 consecutive elements M[s][0..3] at its address,
@@ -35,7 +41,7 @@ struct Swz {
   static constexpr int ROW_BYTES = D * 2;
   // chunk position of chunk c in row r
   __device__ static inline int pos(int r, int c) {
-    if constexpr (D == 128) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
+    if constexpr (D == 128) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
     else return c ^ ((r >> 1) & 7);
   }
   // byte offset of element (r, col) for an 8-byte aligned col group
@@ -62,7 +68,7 @@ __device__ inline void tile_load_lds(char* dst, const __bf16* src, int64_t strid
     const int r = slot / CHUNKS;
     const int cpos = slot % CHUNKS;
     int c = cpos;   // invert the swizzle: the chunk stored at position cpos
-    if constexpr (D == 128) c = cpos ^ (((r & 7) << 1) | ((r >> 3) & 1));
+    if constexpr (D == 128) c = cpos ^ (((r & 3) << 2) | ((r >> 2) & 3));
     else c = cpos ^ ((r >> 1) & 7);
     int32_t row = row0 + r;
     row = row < valid_rows ? row : valid_rows - 1;
