@@ -13,18 +13,23 @@
 //     their K and V rows held in VGPRs as MFMA B operands and their dK^T,
 //     dV^T accumulators in AGPRs) and streams 64-row tiles of Q and dO for
 //     every query head of the GQA group through LDS (direct-to-LDS loads,
-//     double-buffered).  Per tile: S = Q K^T, dP = dO V^T (A operands read
-//     row-wise), P = exp2(S c - LSE log2 e), dS = scale P (dP - Delta), then
-//     dV^T += dO^T P and dK^T += Q^T dS (A operands read with the LDS
-//     transpose read; P and dS go from the accumulator layout straight into
-//     the B operand).  4 MFMA products per (query, key) pair.
+//     double-buffered).  Per tile: S = Q K^T, dP = dO V^T - Delta (A operands
+//     read row-wise; the dP accumulator starts at -Delta), P = exp2(S c + nl)
+//     with nl = -LSE log2 e, dS = P dP, then dV^T += dO^T P and
+//     dK^T += Q^T dS (A operands read with the LDS transpose read; P and dS go
+//     from the accumulator layout straight into the B operand).  4 MFMA
+//     products per (query, key) pair.  The softmax scale of dK is applied once,
+//     at the end.
 //   dq (Q-outer): a work-group owns 64 query rows of 4 query heads sharing a
 //     KV head (like the forward) and streams 64-key tiles of K and V.  Per
 //     tile: S^T = K Q^T, dP^T = V dO^T, P^T, dS^T, dQ^T += K^T dS^T.  3 MFMA
 //     products per pair (S and dP are recomputed rather than exchanged).
-// Fully masked tiles are skipped; element masks only on partial or ragged
-// tiles.  Heavy-first orders: ascending keys for dkdv, descending queries for
-// dq.
+// Both are software-pipelined within a tile: the second half's score MFMAs
+// run beside the first half's exp/dS VALU work, and the first half's gradient
+// MFMAs beside the second half's VALU work (sched_group_barrier).  Masked
+// entries get S = -inf before the exponential, so P = 0; fully masked tiles
+// are skipped and element masks run only on partial or ragged tiles.
+// Heavy-first orders: ascending keys for dkdv, descending queries for dq.
 #include "common.h"
 #include "kernels.h"
 #include "tile_io.h"
@@ -44,84 +49,124 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ inline void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// -LSE * log2(e); an empty row (LSE = -inf) maps to -inf, so that
+// exp2(S c + nl) = 0 for it whatever S is.
+__device__ inline float neg_lse2(float lse) { return lse == -INFINITY ? -INFINITY : -lse * LOG2E; }
+
 // ============================== dK, dV ======================================
 
 template <int D>
 struct KvState {
   bf16x8 kf[D / 16], vf[D / 16];   // this wave's 32 keys as B operands
-  f32x16 dka[D / 32], dva[D / 32]; // dK^T, dV^T accumulators [d block]
+  f32x16 dka[D / 32], dva[D / 32]; // dK^T (unscaled), dV^T accumulators [d block]
   int32_t qlim;                    // queries [qlim, ..) see this lane's key causally
   int32_t kdoc;
   bool kvalid;
 };
 
-// one (64-query tile, head) step for one wave
+// S and dP - Delta of the 32-query block qb of the tile.  Accumulator element
+// r: key = the lane's key, query row qb*32 + 8(r/4) + 4hh + r%4.
 template <int D>
-__device__ inline void dkdv_tile(KvState<D>& st, const char* Qt, const char* Ot, const float* Lt,
-                                 const float* Dlt, const int32_t* QDt, int32_t qa0, int32_t Lq, bool mask,
-                                 bool docs, float c, float scale, int lane) {
+__device__ inline void sdp_block(const KvState<D>& st, const char* Qt, const char* Ot, const float* NDt, int qb,
+                                 f32x16& s, f32x16& dp, int lane) {
   const int lq = lane & 31, hh = lane >> 5;
-  const int s16 = lane & 15, cg = (lane >> 4) & 1;
-  f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+  f32x16 init;   // -Delta of the element's query row
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 d4 = *(const f32x4*)(NDt + qb * 32 + j * 8 + hh * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) init[j * 4 + i] = d4[i];
+  }
+  bf16x8 qa[D / 16], oa[D / 16];
 #pragma unroll
   for (int kd = 0; kd < D / 16; ++kd) {
+    qa[kd] = lds_row8<D>(Qt, qb * 32 + lq, kd * 16 + hh * 8);
+    oa[kd] = lds_row8<D>(Ot, qb * 32 + lq, kd * 16 + hh * 8);
+  }
+  s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0], st.kf[0], f32x16{}, 0, 0, 0);
+  dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[0], st.vf[0], init, 0, 0, 0);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const bf16x8 qa = lds_row8<D>(Qt, qb * 32 + lq, kd * 16 + hh * 8);
-      const bf16x8 oa = lds_row8<D>(Ot, qb * 32 + lq, kd * 16 + hh * 8);
-      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, st.kf[kd], s[qb], 0, 0, 0);
-      dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, st.vf[kd], dp[qb], 0, 0, 0);
+  for (int kd = 1; kd < D / 16; ++kd) {
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kd], st.kf[kd], s, 0, 0, 0);
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[kd], st.vf[kd], dp, 0, 0, 0);
+  }
+}
+
+// Element mask of block qb: S = -inf where the lane's key is not visible.
+template <int D>
+__device__ inline void dkdv_mask(const KvState<D>& st, f32x16& s, const int32_t* QDt, int32_t qa0, int qb,
+                                 int32_t Lq, bool docs, int hh) {
+  asm volatile("; partial tile" ::: "memory");   // keeps the caller's branch real (no if-conversion)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int qr = qb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+    const int32_t qidx = qa0 + qr;
+    const bool ok = st.kvalid & (qidx < Lq) & (qidx >= st.qlim) & (!docs | (QDt[qr] == st.kdoc));
+    s[r] = ok ? s[r] : -INFINITY;
+  }
+}
+
+// P and dS of block qb as B operands (query slots t = 2qb, 2qb + 1).
+__device__ inline void pds_block(const f32x16& s, const f32x16& dp, const float* Nl, int qb, float c,
+                                 bf16x8 (&pf)[2], bf16x8 (&dsf)[2], int hh) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 n4 = *(const f32x4*)(Nl + qb * 32 + j * 8 + hh * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = j * 4 + i;
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, n4[i]));
+      pf[r >> 3][r & 7] = (__bf16)p;
+      dsf[r >> 3][r & 7] = (__bf16)(p * dp[r]);
     }
   }
-  // accumulator element r of block qb: key = lane's key, query row qb*32 + 8(r/4) + 4hh + r%4
-  float p[2][16];
+}
+
+// dV^T += dO^T P, dK^T += Q^T dS over the query slots t0, t0 + 1.
+template <int D>
+__device__ inline void dvdk_block(KvState<D>& st, const char* Qt, const char* Ot, int t0, const bf16x8 (&pf)[2],
+                                  const bf16x8 (&dsf)[2], int lane) {
+  const int hh = lane >> 5, s16 = lane & 15, cg = (lane >> 4) & 1;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 l4 = *(const f32x4*)(Lt + qb * 32 + j * 8 + hh * 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[qb][j * 4 + i] = __builtin_amdgcn_exp2f(fmaf(s[qb][j * 4 + i], c, -l4[i] * LOG2E));
-    }
-  if (mask) {
-    asm volatile("; partial tile" ::: "memory");   // a real branch, not predicated code
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = qb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-        const int32_t qidx = qa0 + qr;
-        const bool ok = st.kvalid & (qidx < Lq) & (qidx >= st.qlim) & (!docs | (QDt[qr] == st.kdoc));
-        p[qb][r] = ok ? p[qb][r] : 0.f;
-      }
-  }
-  bf16x8 pf[4], dsf[4];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 d4 = *(const f32x4*)(Dlt + qb * 32 + j * 8 + hh * 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = j * 4 + i;
-        const float ds = p[qb][r] * (dp[qb][r] - d4[i]) * scale;
-        const int t = qb * 2 + (r >> 3), sl = r & 7;
-        pf[t][sl] = (__bf16)p[qb][r];
-        dsf[t][sl] = (__bf16)ds;
-      }
-    }
-  // dV^T += dO^T P, dK^T += Q^T dS: A operands = transposed reads of the tiles
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int u = 0; u < 2; ++u) {
+    const int t = t0 + u;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int c0 = db * 32 + 16 * cg;
       const bf16x8 oa = cat8(lds_tr4<D>(Ot, 16 * t + 4 * hh, c0, s16), lds_tr4<D>(Ot, 16 * t + 8 + 4 * hh, c0, s16));
       const bf16x8 qa = cat8(lds_tr4<D>(Qt, 16 * t + 4 * hh, c0, s16), lds_tr4<D>(Qt, 16 * t + 8 + 4 * hh, c0, s16));
-      st.dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pf[t], st.dva[db], 0, 0, 0);
-      st.dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsf[t], st.dka[db], 0, 0, 0);
+      st.dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pf[u], st.dva[db], 0, 0, 0);
+      st.dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsf[u], st.dka[db], 0, 0, 0);
     }
   }
+}
+
+// one (64-query tile, head) step for one wave, software-pipelined
+template <int D>
+__device__ inline void dkdv_tile(KvState<D>& st, const char* Qt, const char* Ot, const float* Nl,
+                                 const float* NDt, const int32_t* QDt, int32_t qa0, int32_t Lq, bool mask,
+                                 bool docs, float c, int lane) {
+  const int hh = lane >> 5;
+  f32x16 s0, dp0, s1, dp1;
+  bf16x8 pf0[2], dsf0[2], pf1[2], dsf1[2];
+  sdp_block<D>(st, Qt, Ot, NDt, 0, s0, dp0, lane);
+  if (mask) dkdv_mask<D>(st, s0, QDt, qa0, 0, Lq, docs, hh);
+  __builtin_amdgcn_sched_barrier(0);
+  sdp_block<D>(st, Qt, Ot, NDt, 1, s1, dp1, lane);
+  pds_block(s0, dp0, Nl, 0, c, pf0, dsf0, hh);
+  CP_INTERLEAVE(D / 8, 512 / D);
+  keep_live(pf0);
+  keep_live(dsf0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (mask) dkdv_mask<D>(st, s1, QDt, qa0, 1, Lq, docs, hh);
+  __builtin_amdgcn_sched_barrier(0);
+  dvdk_block<D>(st, Qt, Ot, 0, pf0, dsf0, lane);
+  pds_block(s1, dp1, Nl, 1, c, pf1, dsf1, hh);
+  CP_INTERLEAVE(D / 8, 512 / D);
+  keep_live(pf1);
+  keep_live(dsf1);
+  __builtin_amdgcn_sched_barrier(0);
+  dvdk_block<D>(st, Qt, Ot, 2, pf1, dsf1, lane);
 }
 
 template <int D>
@@ -164,6 +209,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
   const int G = a.G;
   const int nitems = (qt1 - qt0) * G;
 
+  // Q, dO tiles and the rows' LSE, Delta (and doc ids) of item `it`.  The
+  // wave that loaded the LSE (Delta) row converts it in LDS once its loads
+  // have landed (prepare): nl = -LSE log2 e, and -Delta.
   auto issue = [&](int it, char* Qd, char* Od, float* Ld, float* Dd, int32_t* Xd) {
     const int32_t qt = qt0 + it / G;
     const int head = kvh * G + it % G;
@@ -176,6 +224,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
       __builtin_amdgcn_global_load_lds((const void*)(a.delta + (int64_t)head * a.lse_ld + row), CP_LDS_PTR(Dd), 4, 0, 0);
     else if (wave == 2 && docs)
       __builtin_amdgcn_global_load_lds((const void*)(qs.doc + row), CP_LDS_PTR(Xd), 4, 0, 0);
+  };
+  auto prepare = [&](float* Ld, float* Dd) {
+    if (wave == 0) Ld[lane] = neg_lse2(Ld[lane]);
+    else if (wave == 1) Dd[lane] = -Dd[lane];
   };
   if (nitems > 0) issue(0, qb0_, ob0_, lb0_, db0_, xb0_);
 
@@ -205,6 +257,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
   const float c = a.scale * LOG2E;
 
   wait_vm0();
+  if (nitems > 0) prepare(lb0_, db0_);
   __syncthreads();
 
   auto step = [&](int it, const char* Qc, const char* Oc, const float* Lc, const float* Dc, const int32_t* Xc,
@@ -220,8 +273,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
     }
     live = __builtin_amdgcn_readfirstlane((int)live) != 0;   // wave-uniform: scalar branches
     full = __builtin_amdgcn_readfirstlane((int)full) != 0;
-    if (live) dkdv_tile<D>(st, Qc, Oc, Lc, Dc, Xc, qa0, Lq, !full, docs, c, a.scale, lane);
+    if (live) dkdv_tile<D>(st, Qc, Oc, Lc, Dc, Xc, qa0, Lq, !full, docs, c, lane);
     wait_vm0();
+    if (it + 1 < nitems) prepare(Ln, Dn);
     __syncthreads();
   };
   for (int it = 0; it < nitems; it += 2) {
@@ -229,7 +283,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
     if (it + 1 < nitems) step(it + 1, qb1_, ob1_, lb1_, db1_, xb1_, qb0_, ob0_, lb0_, db0_, xb0_);
   }
 
-  // ---- dK, dV (exclusive to this work-group): read-modify-write -------------
+  // ---- dK (scaled here), dV: exclusive to this work-group, read-modify-write --
   if (st.kvalid && wave_has_keys) {
     const int64_t base = ((int64_t)(wk0 + lq) * a.hkv + kvh) * D;
 #pragma unroll
@@ -242,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
         f32x4 ok = *pk, ov = *pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          ok[i] += st.dka[db][4 * j + i];
+          ok[i] += a.scale * st.dka[db][4 * j + i];
           ov[i] += st.dva[db][4 * j + i];
         }
         *pk = ok;
@@ -257,69 +311,107 @@ template <int D>
 struct QState {
   bf16x8 qf[2][D / 16];     // B operands: 64 query rows
   bf16x8 of[2][D / 16];     // B operands: their dO rows
-  f32x16 acc[2][D / 32];    // dQ^T accumulators [query block][d block]
+  f32x16 acc[2][D / 32];    // dQ^T accumulators (unscaled) [query block][d block]
   float nl[2];              // -LSE * log2(e) of the lane's query column
   float dl[2];              // Delta of the lane's query column
   int32_t lim[2];           // keys [0, lim) are causally visible (and < Lk)
   int32_t qdoc[2];
 };
 
+// S^T and dP^T of the 32-key half kb.  Element r of block qb: query = the
+// lane's column of block qb, key = kb*32 + 8(r/4) + 4hh + r%4.
 template <int D>
-__device__ inline void dq_tile(QState<D>& st, const char* Kt, const char* Vt, const int32_t* Dt, int32_t kb0,
-                               bool mask, bool docs, float c, float scale, int lane) {
+__device__ inline void sdp_half(const QState<D>& st, const char* Kt, const char* Vt, int kb, f32x16 (&s)[2],
+                                f32x16 (&dp)[2], int lane) {
   const int lq = lane & 31, hh = lane >> 5;
-  const int s16 = lane & 15, cg = (lane >> 4) & 1;
+  bf16x8 ka[D / 16], va[D / 16];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+  for (int kd = 0; kd < D / 16; ++kd) {
+    ka[kd] = lds_row8<D>(Kt, kb * 32 + lq, kd * 16 + hh * 8);
+    va[kd] = lds_row8<D>(Vt, kb * 32 + lq, kd * 16 + hh * 8);
+  }
 #pragma unroll
-    for (int kd = 0; kd < D / 16; ++kd) {
-      const bf16x8 ka = lds_row8<D>(Kt, kb * 32 + lq, kd * 16 + hh * 8);
-      const bf16x8 va = lds_row8<D>(Vt, kb * 32 + lq, kd * 16 + hh * 8);
+  for (int qb = 0; qb < 2; ++qb) {
+    s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], st.qf[qb][0], f32x16{}, 0, 0, 0);
+    dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], st.of[qb][0], f32x16{}, 0, 0, 0);
+  }
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[qb][kd], s[qb], 0, 0, 0);
-        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, st.of[qb][kd], dp[qb], 0, 0, 0);
-      }
+  for (int kd = 1; kd < D / 16; ++kd)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kd], st.qf[qb][kd], s[qb], 0, 0, 0);
+      dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kd], st.of[qb][kd], dp[qb], 0, 0, 0);
     }
-    // element r of block qb: query = lane's column of block qb, key = kb*32 + 8(r/4) + 4hh + r%4
-    float p[2][16];
+}
+
+template <int D>
+__device__ inline void dq_mask(const QState<D>& st, f32x16 (&s)[2], const int32_t* Dt, int32_t kb0, int kh0, bool docs,
+                               int hh) {
+  asm volatile("; partial tile" ::: "memory");   // keeps the caller's branch real (no if-conversion)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+  for (int r = 0; r < 16; ++r) {
+    const int kk = kh0 + (r >> 2) * 8 + hh * 4 + (r & 3);
+    const int32_t kd_ = Dt[kk];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, st.nl[qb]));
-    if (mask) {
-      asm volatile("; partial tile" ::: "memory");   // a real branch, not predicated code
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-        const int32_t kd_ = Dt[kk];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const bool ok = (kb0 + kk < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
-          p[qb][r] = ok ? p[qb][r] : 0.f;
-        }
-      }
-    }
-    bf16x8 dsf[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dsf[qb][r >> 3][r & 7] = (__bf16)(p[qb][r] * (dp[qb][r] - st.dl[qb]) * scale);
-    // dQ^T[qb][db] += K^T (d rows, 16 keys per step) x dS^T
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int k0 = kb * 32 + 16 * t;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int c0 = db * 32 + 16 * cg;
-        const bf16x8 ka = cat8(lds_tr4<D>(Kt, k0 + 4 * hh, c0, s16), lds_tr4<D>(Kt, k0 + 8 + 4 * hh, c0, s16));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          st.acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsf[qb][t], st.acc[qb][db], 0, 0, 0);
-      }
+    for (int qb = 0; qb < 2; ++qb) {
+      const bool ok = (kb0 + kk < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
+      s[qb][r] = ok ? s[qb][r] : -INFINITY;
     }
   }
+}
+
+template <int D>
+__device__ inline void ds_half(const QState<D>& st, const f32x16 (&s)[2], const f32x16 (&dp)[2], float c,
+                               bf16x8 (&dsf)[2][2]) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, st.nl[qb]));
+      dsf[qb][r >> 3][r & 7] = (__bf16)(p * (dp[qb][r] - st.dl[qb]));
+    }
+}
+
+// dQ^T[qb][db] += K^T (d rows, 16 keys per step) x dS^T for the half kb
+template <int D>
+__device__ inline void dq_half(QState<D>& st, const char* Kt, int kb, const bf16x8 (&dsf)[2][2], int lane) {
+  const int hh = lane >> 5, s16 = lane & 15, cg = (lane >> 4) & 1;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int k0 = kb * 32 + 16 * t;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c0 = db * 32 + 16 * cg;
+      const bf16x8 ka = cat8(lds_tr4<D>(Kt, k0 + 4 * hh, c0, s16), lds_tr4<D>(Kt, k0 + 8 + 4 * hh, c0, s16));
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        st.acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsf[qb][t], st.acc[qb][db], 0, 0, 0);
+    }
+  }
+}
+
+template <int D>
+__device__ inline void dq_tile(QState<D>& st, const char* Kt, const char* Vt, const int32_t* Dt, int32_t kb0,
+                               bool mask, bool docs, float c, int lane) {
+  const int hh = lane >> 5;
+  f32x16 s0[2], dp0[2], s1[2], dp1[2];
+  bf16x8 ds0[2][2], ds1[2][2];
+  sdp_half<D>(st, Kt, Vt, 0, s0, dp0, lane);
+  if (mask) dq_mask<D>(st, s0, Dt, kb0, 0, docs, hh);
+  __builtin_amdgcn_sched_barrier(0);
+  sdp_half<D>(st, Kt, Vt, 1, s1, dp1, lane);
+  ds_half<D>(st, s0, dp0, c, ds0);
+  CP_INTERLEAVE(D / 4, 5);
+  keep_live(ds0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (mask) dq_mask<D>(st, s1, Dt, kb0, 32, docs, hh);
+  __builtin_amdgcn_sched_barrier(0);
+  dq_half<D>(st, Kt, 0, ds0, lane);
+  ds_half<D>(st, s1, dp1, c, ds1);
+  CP_INTERLEAVE(D / 8, 9);
+  keep_live(ds1);
+  __builtin_amdgcn_sched_barrier(0);
+  dq_half<D>(st, Kt, 1, ds1, lane);
 }
 
 template <int D>
@@ -388,7 +480,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
     }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) st.acc[qb][db] = f32x16{};
-    st.nl[qb] = -a.lse[(int64_t)head * a.lse_ld + row] * LOG2E;
+    st.nl[qb] = neg_lse2(a.lse[(int64_t)head * a.lse_ld + row]);
     st.dl[qb] = a.delta[(int64_t)head * a.lse_ld + row];
     st.lim[qb] = causal ? min(Lk, span_count_le(ks, span_pos(qs, row))) : Lk;
     st.qdoc[qb] = docs ? qs.doc[row] : 0;
@@ -414,7 +506,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
     }
     live = __builtin_amdgcn_readfirstlane((int)live) != 0;   // wave-uniform: scalar branches
     full = __builtin_amdgcn_readfirstlane((int)full) != 0;
-    if (live) dq_tile<D>(st, Kc, Vc, Xc, kb0, !full, docs, c, a.scale, lane);
+    if (live) dq_tile<D>(st, Kc, Vc, Xc, kb0, !full, docs, c, lane);
     wait_vm0();
     __syncthreads();
   };
@@ -436,7 +528,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
           f32x4* p = (f32x4*)(dst + db * 32 + j * 8 + hh * 4);
           f32x4 v = *p;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] += st.acc[qb][db][4 * j + i];
+          for (int i = 0; i < 4; ++i) v[i] += a.scale * st.acc[qb][db][4 * j + i];
           *p = v;
         }
     }

@@ -158,6 +158,126 @@ __device__ inline float fwd_accumulate(FwdState<D>& st, const char* Vt, const f3
   return fmaxf(tsum[0], tsum[1]);
 }
 
+// ---- software-pipelined tile (full tiles, reference point set) -------------
+// Per 64-key tile: S0 = QK(keys 0..31); then S1 = QK(keys 32..63) interleaved
+// with exp(S0); then O += V0 P0 interleaved with exp(S1); then O += V1 P1.
+// The interleaving (1 MFMA, then VALU work, repeated) lets the VALU softmax run
+// while the matrix core executes the independent MFMAs; it is imposed with
+// sched_group_barrier because the scheduler would otherwise cluster them.
+
+template <int D>
+__device__ inline void qk_half(const FwdState<D>& st, const char* Kt, int kb, f32x16 (&s)[2], int lane) {
+  const int lq = lane & 31, hh = lane >> 5;
+  bf16x8 ka[D / 16];
+#pragma unroll
+  for (int kd = 0; kd < D / 16; ++kd) ka[kd] = lds_row8<D>(Kt, kb * 32 + lq, kd * 16 + hh * 8);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], st.qf[qb][0], f32x16{}, 0, 0, 0);
+#pragma unroll
+  for (int kd = 1; kd < D / 16; ++kd)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kd], st.qf[qb][kd], s[qb], 0, 0, 0);
+}
+
+template <int D>
+__device__ inline void exp_half(const FwdState<D>& st, const f32x16 (&s)[2], bf16x8 (&pf)[2][2], float (&tsum)[2],
+                                float c) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][t * 8 + i], c, st.moff[qb]));
+        tsum[qb] += p;
+        pf[qb][t][i] = (__bf16)p;
+      }
+}
+
+template <int D>
+__device__ inline void pv_half(FwdState<D>& st, const char* Vt, int kb, const bf16x8 (&pf)[2][2], int lane) {
+  const int hh = lane >> 5, s16 = lane & 15, cg = (lane >> 4) & 1;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int k0 = kb * 32 + 16 * t;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c0 = db * 32 + 16 * cg;
+      const bf16x8 va = cat8(lds_tr4<D>(Vt, k0 + 4 * hh, c0, s16), lds_tr4<D>(Vt, k0 + 8 + 4 * hh, c0, s16));
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        st.oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][t], st.oacc[qb][db], 0, 0, 0);
+    }
+  }
+}
+
+
+// Element mask of one 32-key half (keys kh0.. of the tile).
+template <int D>
+__device__ inline void mask_half(const FwdState<D>& st, f32x16 (&s)[2], const int32_t* Dt, int32_t kb0, int kh0,
+                                 bool docs, int hh) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int kk = kh0 + (r >> 2) * 8 + hh * 4 + (r & 3);
+    const int32_t kidx = kb0 + kk;
+    const int32_t kd_ = Dt[kk];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const bool ok = (kidx < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
+      s[qb][r] = ok ? s[qb][r] : -INFINITY;
+    }
+  }
+}
+
+// Rows that have no reference point yet take the max of this half's scores
+// (their accumulators and sums are still zero, so nothing is rescaled).
+template <int D>
+__device__ inline void init_half(FwdState<D>& st, const f32x16 (&s)[2], float c) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float m0 = fmaxf(s[qb][0], s[qb][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) m0 = fmaxf(m0, fmaxf(s[qb][r], s[qb][r + 1]));
+    m0 = fmaxf(m0, __shfl_xor(m0, 32));
+    if (st.mrow[qb] == -INFINITY && m0 != -INFINITY) {
+      st.mrow[qb] = m0;
+      st.moff[qb] = -m0 * c;
+    }
+  }
+}
+
+// One 64-key tile, one code path for all tiles (the same registers carry the
+// accumulators throughout): partial tiles insert the mask and tiles with
+// unset reference points insert the init between the pipeline stages.
+template <int D>
+__device__ inline float fwd_tile_piped(FwdState<D>& st, const char* Kt, const char* Vt, const int32_t* Dt,
+                                       int32_t kb0, bool full, bool docs, float c, int lane) {
+  const int hh = lane >> 5;
+  f32x16 s0[2], s1[2];
+  bf16x8 p0[2][2], p1[2][2];
+  float tsum[2] = {0.f, 0.f};
+  qk_half<D>(st, Kt, 0, s0, lane);
+  if (!full) mask_half<D>(st, s0, Dt, kb0, 0, docs, hh);
+  if (__any((st.mrow[0] == -INFINITY) | (st.mrow[1] == -INFINITY))) init_half<D>(st, s0, c);
+  __builtin_amdgcn_sched_barrier(0);
+  qk_half<D>(st, Kt, 1, s1, lane);
+  exp_half<D>(st, s0, p0, tsum, c);
+  CP_INTERLEAVE(D / 8, 7);
+  keep_live(p0);   // P0 must be computed here, next to QK1, not sunk past the branches below
+  __builtin_amdgcn_sched_barrier(0);
+  if (!full) mask_half<D>(st, s1, Dt, kb0, 32, docs, hh);
+  if (__any((st.mrow[0] == -INFINITY) | (st.mrow[1] == -INFINITY))) init_half<D>(st, s1, c);
+  __builtin_amdgcn_sched_barrier(0);
+  pv_half<D>(st, Vt, 0, p0, lane);
+  exp_half<D>(st, s1, p1, tsum, c);
+  CP_INTERLEAVE(D / 8, 7);
+  __builtin_amdgcn_sched_barrier(0);
+  pv_half<D>(st, Vt, 1, p1, lane);
+  st.lrow[0] += tsum[0];
+  st.lrow[1] += tsum[1];
+  return fmaxf(tsum[0], tsum[1]);
+}
+
 // Exact online softmax for one tile (the fallback path): running max and
 // rescaling of the accumulators whenever the max rises.
 template <int D>
@@ -291,29 +411,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
     if (kt + 1 < kt1) issue(kt + 1, Kn, Vn, Dn);
     bool live, full;
     classify(kt, Dc, live, full);
-    if (live) {
-      f32x16 s[2][2];
-      fwd_scores<D>(st, Kc, s, lane);
-      if (!full) {
-        asm volatile("; partial tile" ::: "memory");   // a real branch, not predicated code
-        fwd_mask<D>(st, s, Dc, kt * BK, docs, hh);
-      }
-      if (__builtin_expect(__any((st.mrow[0] == -INFINITY) | (st.mrow[1] == -INFINITY)), 0)) {
-        // rows without a reference point yet take this tile's max (their
-        // accumulators are still zero, so nothing is rescaled)
-        asm volatile("; first tile" ::: "memory");
-        float mx[2];
-        fwd_tile_max(s, mx);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          if (st.mrow[qb] == -INFINITY && mx[qb] != -INFINITY) {
-            st.mrow[qb] = mx[qb];
-            st.moff[qb] = -mx[qb] * c;
-          }
-        }
-      }
-      worst = fmaxf(worst, fwd_accumulate<D>(st, Vc, s, c, lane));
-    }
+    if (live) worst = fmaxf(worst, fwd_tile_piped<D>(st, Kc, Vc, Dc, kt * BK, full, docs, c, lane));
     wait_vm0();
     __syncthreads();
   };

@@ -100,4 +100,33 @@ __device__ inline bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// ---- instruction-scheduling helpers ----------------------------------------
+// Interleave n MFMAs with v VALU instructions after each (sched_group_barrier
+// masks: 0x008 MFMA, 0x002 VALU).  Used where a stage's MFMAs are independent
+// of the VALU work placed next to them, so the VALU runs while the matrix core
+// is busy; without it the scheduler clusters the two kinds.
+#define CP_INTERLEAVE(n, v)                                   \
+  do {                                                        \
+    _Pragma("unroll") for (int i_ = 0; i_ < (n); ++i_) {      \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      \
+      __builtin_amdgcn_sched_group_barrier(0x002, (v), 0);    \
+    }                                                         \
+  } while (0)
+
+// Pin values in place: an empty asm that reads them, so the compiler cannot
+// sink their computation into a later block (which would undo an
+// interleaving above it).
+template <int A, int B>
+__device__ inline void keep_live(const bf16x8 (&p)[A][B]) {
+#pragma unroll
+  for (int a = 0; a < A; ++a)
+#pragma unroll
+    for (int b = 0; b < B; ++b) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, p[a][b])));
+}
+template <int A>
+__device__ inline void keep_live(const bf16x8 (&p)[A]) {
+#pragma unroll
+  for (int a = 0; a < A; ++a) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, p[a])));
+}
+
 }  // namespace cp
