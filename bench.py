@@ -186,12 +186,55 @@ def kernel_times(wl, cp, torch, iters):
     torch.cuda.synchronize()
     ms = [ev[i].elapsed_time(ev[i + 1]) / iters for i in range(4)]
     rh = wl.rows * wl.hq
+    # Algorithmic FLOPs per launch (2*d per live pair per Q head per GEMM):
+    # the forward's 2 GEMMs; the backward's 5 GEMMs split as dK/dV kernel =
+    # S recompute, dP, dV, dK (4) and dQ kernel = dQ (1).  The dQ kernel also
+    # recomputes S and dP (executed, not algorithmic).
+    unit = 2 * wl.d * pairs * wl.hq
     return {
-        "fwd_bf16_kernel": {"ms": ms[0], "flops": 4 * wl.d * pairs * wl.hq},
-        "dkdv_bf16_kernel": {"ms": ms[1], "flops": 8 * wl.d * pairs * wl.hq},
-        "dq_bf16_kernel": {"ms": ms[2], "flops": 6 * wl.d * pairs * wl.hq},
+        "fwd_bf16_kernel": {"ms": ms[0], "flops": 2 * unit, "flops_executed": 2 * unit},
+        "dkdv_bf16_kernel": {"ms": ms[1], "flops": 4 * unit, "flops_executed": 4 * unit},
+        "dq_bf16_kernel": {"ms": ms[2], "flops": 1 * unit, "flops_executed": 3 * unit},
         "merge_kernel": {"ms": ms[3], "bytes": rh * (3 * wl.d * 4 + 3 * 4)},
     }
+
+
+# Source files each hot kernel is compiled from: a traffic figure measured
+# with rocprofv3 counters is reported only while these are unchanged.
+KERNEL_SOURCES = {
+    "dkdv_bf16_kernel": ["attn_bwd_bf16.hip", "tile_io.h", "common.h", "kernels.h"],
+    "dq_bf16_kernel": ["attn_bwd_bf16.hip", "tile_io.h", "common.h", "kernels.h"],
+    "fwd_bf16_kernel": ["attn_fwd_bf16.hip", "tile_io.h", "common.h", "kernels.h"],
+}
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "sequence_context_parallelism_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary profiles/traffic_<kernel>_<workload>.txt (FETCH_SIZE and
+    WRITE_SIZE per dispatch, scaled by the same counters' reading for a plain
+    copy of known size), or None if there is none or the kernel's sources have
+    changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("source_sha256_16") != kernel_source_hash(kernel):
+        return None
+    return float(kv["hbm_bytes_per_launch"])
 
 
 def sampled_parity(wl, torch):
@@ -221,11 +264,11 @@ def sampled_parity(wl, torch):
 
 def cpu_baseline(wl):
     """The oracle (untuned) on the host cores: forward + backward of one KV
-    group (hq/hkv query heads sharing one KV head) over the first 8192 tokens
+    group (hq/hkv query heads sharing one KV head) over the first 16384 tokens
     of the causal sequence, in causal-FLOP TFLOPS."""
     import torch
     from oracle import attention as A
-    L = 8192
+    L = 16384
     g = wl.hq // wl.hkv
     q = wl.q[:L, :g].float().cpu().numpy()
     k = wl.k[:L, :1].float().cpu().numpy()
@@ -312,16 +355,20 @@ def main():
             e = {"ms": round(r["ms"], 4)}
             if "flops" in r:
                 e["tflops"] = round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 1)
+                e["tflops_executed"] = round(r["flops_executed"] / (r["ms"] * 1e-3) / 1e12, 1)
             else:
                 e["gb_s"] = round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1)
                 e["frac_hbm_8tbs"] = round(r["bytes"] / (r["ms"] * 1e-3) / 8e12, 3)
             out["kernels"][name] = e
         dom = max((n for n in kt if "flops" in kt[n]), key=lambda n: kt[n]["ms"])
         ach = kt[dom]["flops"] / (kt[dom]["ms"] * 1e-3) / 1e12
+        traffic = measured_traffic(dom, args.workload)
         out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                           "flops_per_launch": kt[dom]["flops"], "ms_per_launch": round(kt[dom]["ms"], 4)}
+                           "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                           "traffic": None if traffic is None else round(traffic),
+                           "flops_per_launch": kt[dom]["flops"], "ms_per_launch": round(kt[dom]["ms"], 4),
+                           "source_sha256_16": kernel_source_hash(dom)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

@@ -349,3 +349,29 @@ def test_planted_mistakes_are_caught(monkeypatch):
     fin = np.isfinite(l1) & np.isfinite(l2)
     bo, _ = bad_merge(o1, l1, o2, l2)
     assert np.max(np.abs((bo - ob)[fin.T])) > 1e-6
+
+    # interleaved GQA head map (h mod Hkv) instead of contiguous groups
+    q2, k2, v2, qp2, kp2, _, _ = _case(rng, 6, 6, 4, 2, 3, False)
+    ob2, _ = brute_force(q2, k2, v2, qp2, kp2, 0.5, True)
+    monkeypatch.setattr(A, "kv_head", lambda h, hq, hkv: h % hkv)
+    o2b, _ = A.forward(q2, k2, v2, qp2, kp2, scale=0.5, causal=True)
+    monkeypatch.undo()
+    assert np.max(np.abs(o2b - ob2)) > 1e-6
+
+    # wrong sign of Delta (dS = P (dP + Delta)): the gradient leaves the
+    # finite-difference value
+    o3, l3 = A.forward(q, k, v, qpos, kpos, scale=0.5, causal=True)
+    dout = rng.standard_normal(o3.shape)
+    good = A.delta(o3, dout)
+    dq_bad, _, _ = A.backward(q, k, v, dout, l3, -good, qpos, kpos, scale=0.5, causal=True)
+    eps, idx = 1e-5, (3, 1, 2)
+    old = q[idx]
+    q[idx] = old + eps
+    fp = _loss(q, k, v, dout, qpos, kpos, 0.5, None, None)
+    q[idx] = old - eps
+    fm = _loss(q, k, v, dout, qpos, kpos, 0.5, None, None)
+    q[idx] = old
+    dq_good, _, _ = A.backward(q, k, v, dout, l3, good, qpos, kpos, scale=0.5, causal=True)
+    num = (fp - fm) / (2 * eps)
+    assert abs(dq_good[idx] - num) <= 1e-8
+    assert abs(dq_bad[idx] - num) > 1e-6
