@@ -30,6 +30,7 @@
 // entries get S = -inf before the exponential, so P = 0; fully masked tiles
 // are skipped and element masks run only on partial or ragged tiles.
 // Heavy-first orders: ascending keys for dkdv, descending queries for dq.
+// Inside a dkdv work-group the query tiles run from the last one down.
 #include "common.h"
 #include "kernels.h"
 #include "tile_io.h"
@@ -209,11 +210,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
   const int G = a.G;
   const int nitems = (qt1 - qt0) * G;
 
+  // Item `it` = (query tile, head), query tiles in DESCENDING order: the
+  // work-groups resident on one XCD hold different key blocks of the same KV
+  // head, so starting them all at the last query tile has them read the same
+  // Q/dO tiles at about the same time (L2 hits instead of HBM re-reads).
   // Q, dO tiles and the rows' LSE, Delta (and doc ids) of item `it`.  The
   // wave that loaded the LSE (Delta) row converts it in LDS once its loads
   // have landed (prepare): nl = -LSE log2 e, and -Delta.
   auto issue = [&](int it, char* Qd, char* Od, float* Ld, float* Dd, int32_t* Xd) {
-    const int32_t qt = qt0 + it / G;
+    const int32_t qt = qt1 - 1 - it / G;
     const int head = kvh * G + it % G;
     tile_load_lds<D, BQ, 4>(Qd, a.q + (int64_t)head * D, a.q_stride, qt * BQ, Lq, wave, lane);
     tile_load_lds<D, BQ, 4>(Od, a.dout + (int64_t)head * D, (int64_t)a.hq * D, qt * BQ, Lq, wave, lane);
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
   auto step = [&](int it, const char* Qc, const char* Oc, const float* Lc, const float* Dc, const int32_t* Xc,
                   char* Qn, char* On, float* Ln, float* Dn, int32_t* Xn) {
     if (it + 1 < nitems) issue(it + 1, Qn, On, Ln, Dn, Xn);
-    const int32_t qa0 = (qt0 + it / G) * BQ, qa1 = min(Lq, qa0 + BQ);
+    const int32_t qa0 = (qt1 - 1 - it / G) * BQ, qa1 = min(Lq, qa0 + BQ);
     bool live = wave_has_keys && qa1 - 1 >= q_none;
     bool full = qa1 - qa0 == BQ && qa0 >= q_all && wk1 - wk0 == BKW;
     if (docs) {
