@@ -50,6 +50,10 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ inline void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+__device__ inline f32x4 lds_f4(uint32_t a) { return *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)a; }
+__device__ inline float lds_ldf(uint32_t a) { return *(const __attribute__((address_space(3))) float*)(uintptr_t)a; }
+__device__ inline void lds_stf(uint32_t a, float x) { *(__attribute__((address_space(3))) float*)(uintptr_t)a = x; }
+
 // -LSE * log2(e); an empty row (LSE = -inf) maps to -inf, so that
 // exp2(S c + nl) = 0 for it whatever S is.
 __device__ inline float neg_lse2(float lse) { return lse == -INFINITY ? -INFINITY : -lse * LOG2E; }
@@ -68,51 +72,45 @@ struct KvState {
 // S and dP - Delta of the 32-query block qb of the tile.  Accumulator element
 // r: key = the lane's key, query row qb*32 + 8(r/4) + 4hh + r%4.
 template <int D>
-__device__ inline void sdp_block(const KvState<D>& st, const char* Qt, const char* Ot, const float* NDt, int qb,
-                                 f32x16& s, f32x16& dp, int lane) {
-  const int lq = lane & 31, hh = lane >> 5;
+__device__ inline void sdp_block(const KvState<D>& st, const RowReader<D>& rr, uint32_t Qt, uint32_t Ot,
+                                 uint32_t NDt, int qb, f32x16& s, f32x16& dp, int lane) {
+  const int hh = lane >> 5;
   f32x16 init;   // -Delta of the element's query row
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const f32x4 d4 = *(const f32x4*)(NDt + qb * 32 + j * 8 + hh * 4);
+    const f32x4 d4 = lds_f4(NDt + 4 * (qb * 32 + j * 8 + hh * 4));
 #pragma unroll
     for (int i = 0; i < 4; ++i) init[j * 4 + i] = d4[i];
   }
-  bf16x8 qa[D / 16], oa[D / 16];
-#pragma unroll
-  for (int kd = 0; kd < D / 16; ++kd) {
-    qa[kd] = lds_row8<D>(Qt, qb * 32 + lq, kd * 16 + hh * 8);
-    oa[kd] = lds_row8<D>(Ot, qb * 32 + lq, kd * 16 + hh * 8);
-  }
-  s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0], st.kf[0], f32x16{}, 0, 0, 0);
-  dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[0], st.vf[0], init, 0, 0, 0);
+  s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Qt, qb, 0), st.kf[0], f32x16{}, 0, 0, 0);
+  dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Ot, qb, 0), st.vf[0], init, 0, 0, 0);
 #pragma unroll
   for (int kd = 1; kd < D / 16; ++kd) {
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kd], st.kf[kd], s, 0, 0, 0);
-    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[kd], st.vf[kd], dp, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Qt, qb, kd), st.kf[kd], s, 0, 0, 0);
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Ot, qb, kd), st.vf[kd], dp, 0, 0, 0);
   }
 }
 
 // Element mask of block qb: S = -inf where the lane's key is not visible.
 template <int D>
-__device__ inline void dkdv_mask(const KvState<D>& st, f32x16& s, const int32_t* QDt, int32_t qa0, int qb,
+__device__ inline void dkdv_mask(const KvState<D>& st, f32x16& s, uint32_t QDt, int32_t qa0, int qb,
                                  int32_t Lq, bool docs, int hh) {
   asm volatile("; partial tile" ::: "memory");   // keeps the caller's branch real (no if-conversion)
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int qr = qb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
     const int32_t qidx = qa0 + qr;
-    const bool ok = st.kvalid & (qidx < Lq) & (qidx >= st.qlim) & (!docs | (QDt[qr] == st.kdoc));
+    const bool ok = st.kvalid & (qidx < Lq) & (qidx >= st.qlim) & (!docs | (lds_ld4i(QDt + 4 * qr) == st.kdoc));
     s[r] = ok ? s[r] : -INFINITY;
   }
 }
 
 // P and dS of block qb as B operands (query slots t = 2qb, 2qb + 1).
-__device__ inline void pds_block(const f32x16& s, const f32x16& dp, const float* Nl, int qb, float c,
+__device__ inline void pds_block(const f32x16& s, const f32x16& dp, uint32_t Nl, int qb, float c,
                                  bf16x8 (&pf)[2], bf16x8 (&dsf)[2], int hh) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const f32x4 n4 = *(const f32x4*)(Nl + qb * 32 + j * 8 + hh * 4);
+    const f32x4 n4 = lds_f4(Nl + 4 * (qb * 32 + j * 8 + hh * 4));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = j * 4 + i;
@@ -125,64 +123,62 @@ __device__ inline void pds_block(const f32x16& s, const f32x16& dp, const float*
 
 // dV^T += dO^T P, dK^T += Q^T dS over the query slots t0, t0 + 1.
 template <int D>
-__device__ inline void dvdk_block(KvState<D>& st, const char* Qt, const char* Ot, int t0, const bf16x8 (&pf)[2],
-                                  const bf16x8 (&dsf)[2], int lane) {
-  const int hh = lane >> 5, s16 = lane & 15, cg = (lane >> 4) & 1;
+__device__ inline void dvdk_block(KvState<D>& st, const TrReader<D>& tr, uint32_t Qt, uint32_t Ot, int t0,
+                                  const bf16x8 (&pf)[2], const bf16x8 (&dsf)[2]) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int t = t0 + u;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int c0 = db * 32 + 16 * cg;
-      const bf16x8 oa = cat8(lds_tr4<D>(Ot, 16 * t + 4 * hh, c0, s16), lds_tr4<D>(Ot, 16 * t + 8 + 4 * hh, c0, s16));
-      const bf16x8 qa = cat8(lds_tr4<D>(Qt, 16 * t + 4 * hh, c0, s16), lds_tr4<D>(Qt, 16 * t + 8 + 4 * hh, c0, s16));
-      st.dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pf[u], st.dva[db], 0, 0, 0);
-      st.dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsf[u], st.dka[db], 0, 0, 0);
+      st.dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr.at(Ot, 16 * t, db), pf[u], st.dva[db], 0, 0, 0);
+      st.dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr.at(Qt, 16 * t, db), dsf[u], st.dka[db], 0, 0, 0);
     }
   }
 }
 
 // one (64-query tile, head) step for one wave, software-pipelined
 template <int D>
-__device__ inline void dkdv_tile(KvState<D>& st, const char* Qt, const char* Ot, const float* Nl,
-                                 const float* NDt, const int32_t* QDt, int32_t qa0, int32_t Lq, bool mask,
-                                 bool docs, float c, int lane) {
+__device__ inline void dkdv_tile(KvState<D>& st, const RowReader<D>& rr, const TrReader<D>& tr, uint32_t Qt,
+                                 uint32_t Ot, uint32_t Nl, uint32_t NDt, uint32_t QDt, int32_t qa0, int32_t Lq,
+                                 bool mask, bool docs, float c, int lane) {
   const int hh = lane >> 5;
   f32x16 s0, dp0, s1, dp1;
   bf16x8 pf0[2], dsf0[2], pf1[2], dsf1[2];
-  sdp_block<D>(st, Qt, Ot, NDt, 0, s0, dp0, lane);
+  // Stage LDS reads: sdp_block = 4 (-Delta) + D/8 row reads for D/8 MFMAs;
+  // pds_block = 4 (nl); dvdk_block = 2 transposed reads per MFMA.
+  sdp_block<D>(st, rr, Qt, Ot, NDt, 0, s0, dp0, lane);
+  CP_PIPE(10, D / 8, 0, 1);
+  __builtin_amdgcn_sched_barrier(0);
   if (mask) dkdv_mask<D>(st, s0, QDt, qa0, 0, Lq, docs, hh);
   __builtin_amdgcn_sched_barrier(0);
-  sdp_block<D>(st, Qt, Ot, NDt, 1, s1, dp1, lane);
+  sdp_block<D>(st, rr, Qt, Ot, NDt, 1, s1, dp1, lane);
   pds_block(s0, dp0, Nl, 0, c, pf0, dsf0, hh);
-  CP_INTERLEAVE(D / 8, 512 / D);
+  CP_PIPE(14, D / 8, 512 / D, 1);
   keep_live(pf0);
   keep_live(dsf0);
   __builtin_amdgcn_sched_barrier(0);
   if (mask) dkdv_mask<D>(st, s1, QDt, qa0, 1, Lq, docs, hh);
   __builtin_amdgcn_sched_barrier(0);
-  dvdk_block<D>(st, Qt, Ot, 0, pf0, dsf0, lane);
+  dvdk_block<D>(st, tr, Qt, Ot, 0, pf0, dsf0);
   pds_block(s1, dp1, Nl, 1, c, pf1, dsf1, hh);
-  CP_INTERLEAVE(D / 8, 512 / D);
+  CP_PIPE(8, D / 8, 512 / D, 2);
   keep_live(pf1);
   keep_live(dsf1);
   __builtin_amdgcn_sched_barrier(0);
-  dvdk_block<D>(st, Qt, Ot, 2, pf1, dsf1, lane);
+  dvdk_block<D>(st, tr, Qt, Ot, 2, pf1, dsf1);
+  CP_PIPE(4, D / 8, 0, 2);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
-  constexpr int TB = BQ * D * 2;
-  __shared__ __attribute__((aligned(16))) char qb0_[TB];
-  __shared__ __attribute__((aligned(16))) char qb1_[TB];
-  __shared__ __attribute__((aligned(16))) char ob0_[TB];
-  __shared__ __attribute__((aligned(16))) char ob1_[TB];
-  __shared__ __attribute__((aligned(16))) float lb0_[BQ];
-  __shared__ __attribute__((aligned(16))) float lb1_[BQ];
-  __shared__ __attribute__((aligned(16))) float db0_[BQ];
-  __shared__ __attribute__((aligned(16))) float db1_[BQ];
-  __shared__ __attribute__((aligned(16))) int32_t xb0_[BQ];
-  __shared__ __attribute__((aligned(16))) int32_t xb1_[BQ];
+  // LDS arena: Q and dO tiles (double-buffered), then per-row LSE (as
+  // -LSE log2 e), -Delta and doc ids, each double-buffered.
+  constexpr uint32_t TB = BQ * D * 2, RW = BQ * 4;
+  constexpr uint32_t Q0 = 0, Q1 = TB, O0 = 2 * TB, O1 = 3 * TB;
+  constexpr uint32_t L0 = 4 * TB, L1 = L0 + RW, N0 = L1 + RW, N1 = N0 + RW, X0 = N1 + RW, X1 = X0 + RW;
+  __shared__ __attribute__((aligned(16))) char smem[X1 + RW];
+  const uint32_t S0 = lds_addr(smem);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hh = lane >> 5;
@@ -217,24 +213,24 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
   // Q, dO tiles and the rows' LSE, Delta (and doc ids) of item `it`.  The
   // wave that loaded the LSE (Delta) row converts it in LDS once its loads
   // have landed (prepare): nl = -LSE log2 e, and -Delta.
-  auto issue = [&](int it, char* Qd, char* Od, float* Ld, float* Dd, int32_t* Xd) {
+  auto issue = [&](int it, uint32_t Qd, uint32_t Od, uint32_t Ld, uint32_t Dd, uint32_t Xd) {
     const int32_t qt = qt1 - 1 - it / G;
     const int head = kvh * G + it % G;
     tile_load_lds<D, BQ, 4>(Qd, a.q + (int64_t)head * D, a.q_stride, qt * BQ, Lq, wave, lane);
     tile_load_lds<D, BQ, 4>(Od, a.dout + (int64_t)head * D, (int64_t)a.hq * D, qt * BQ, Lq, wave, lane);
     const int32_t row = min(qt * BQ + lane, Lq - 1);
     if (wave == 0)
-      __builtin_amdgcn_global_load_lds((const void*)(a.lse + (int64_t)head * a.lse_ld + row), CP_LDS_PTR(Ld), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(a.lse + (int64_t)head * a.lse_ld + row), CP_LDS_AT(Ld), 4, 0, 0);
     else if (wave == 1)
-      __builtin_amdgcn_global_load_lds((const void*)(a.delta + (int64_t)head * a.lse_ld + row), CP_LDS_PTR(Dd), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(a.delta + (int64_t)head * a.lse_ld + row), CP_LDS_AT(Dd), 4, 0, 0);
     else if (wave == 2 && docs)
-      __builtin_amdgcn_global_load_lds((const void*)(qs.doc + row), CP_LDS_PTR(Xd), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(qs.doc + row), CP_LDS_AT(Xd), 4, 0, 0);
   };
-  auto prepare = [&](float* Ld, float* Dd) {
-    if (wave == 0) Ld[lane] = neg_lse2(Ld[lane]);
-    else if (wave == 1) Dd[lane] = -Dd[lane];
+  auto prepare = [&](uint32_t Ld, uint32_t Dd) {
+    if (wave == 0) lds_stf(Ld + 4 * lane, neg_lse2(lds_ldf(Ld + 4 * lane)));
+    else if (wave == 1) lds_stf(Dd + 4 * lane, -lds_ldf(Dd + 4 * lane));
   };
-  if (nitems > 0) issue(0, qb0_, ob0_, lb0_, db0_, xb0_);
+  if (nitems > 0) issue(0, S0 + Q0, S0 + O0, S0 + L0, S0 + N0, S0 + X0);
 
   KvState<D> st;
   {
@@ -261,31 +257,35 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
   const int32_t kd_hi = docs ? ks.doc[wlast] : 0;
   const float c = a.scale * LOG2E;
 
+  const RowReader<D> rr(lane);
+  const TrReader<D> tr(lane);
+
   wait_vm0();
-  if (nitems > 0) prepare(lb0_, db0_);
+  if (nitems > 0) prepare(S0 + L0, S0 + N0);
   __syncthreads();
 
-  auto step = [&](int it, const char* Qc, const char* Oc, const float* Lc, const float* Dc, const int32_t* Xc,
-                  char* Qn, char* On, float* Ln, float* Dn, int32_t* Xn) {
+  auto step = [&](int it, uint32_t Qc, uint32_t Oc, uint32_t Lc, uint32_t Dc, uint32_t Xc, uint32_t Qn,
+                  uint32_t On, uint32_t Ln, uint32_t Dn, uint32_t Xn) {
     if (it + 1 < nitems) issue(it + 1, Qn, On, Ln, Dn, Xn);
     const int32_t qa0 = (qt1 - 1 - it / G) * BQ, qa1 = min(Lq, qa0 + BQ);
     bool live = wave_has_keys && qa1 - 1 >= q_none;
     bool full = qa1 - qa0 == BQ && qa0 >= q_all && wk1 - wk0 == BKW;
     if (docs) {
-      const int32_t qd_lo = Xc[0], qd_hi = Xc[qa1 - qa0 - 1];
+      const int32_t qd_lo = lds_ld4i(Xc), qd_hi = lds_ld4i(Xc + 4 * (qa1 - qa0 - 1));
       live = live && kd_hi >= qd_lo && kd_lo <= qd_hi;
       full = full && qd_lo == qd_hi && kd_lo == kd_hi && kd_lo == qd_lo;
     }
     live = __builtin_amdgcn_readfirstlane((int)live) != 0;   // wave-uniform: scalar branches
     full = __builtin_amdgcn_readfirstlane((int)full) != 0;
-    if (live) dkdv_tile<D>(st, Qc, Oc, Lc, Dc, Xc, qa0, Lq, !full, docs, c, lane);
+    if (live) dkdv_tile<D>(st, rr, tr, Qc, Oc, Lc, Dc, Xc, qa0, Lq, !full, docs, c, lane);
     wait_vm0();
     if (it + 1 < nitems) prepare(Ln, Dn);
     __syncthreads();
   };
   for (int it = 0; it < nitems; it += 2) {
-    step(it, qb0_, ob0_, lb0_, db0_, xb0_, qb1_, ob1_, lb1_, db1_, xb1_);
-    if (it + 1 < nitems) step(it + 1, qb1_, ob1_, lb1_, db1_, xb1_, qb0_, ob0_, lb0_, db0_, xb0_);
+    step(it, S0 + Q0, S0 + O0, S0 + L0, S0 + N0, S0 + X0, S0 + Q1, S0 + O1, S0 + L1, S0 + N1, S0 + X1);
+    if (it + 1 < nitems)
+      step(it + 1, S0 + Q1, S0 + O1, S0 + L1, S0 + N1, S0 + X1, S0 + Q0, S0 + O0, S0 + L0, S0 + N0, S0 + X0);
   }
 
   // ---- dK (scaled here), dV: exclusive to this work-group, read-modify-write --
@@ -326,37 +326,27 @@ struct QState {
 // S^T and dP^T of the 32-key half kb.  Element r of block qb: query = the
 // lane's column of block qb, key = kb*32 + 8(r/4) + 4hh + r%4.
 template <int D>
-__device__ inline void sdp_half(const QState<D>& st, const char* Kt, const char* Vt, int kb, f32x16 (&s)[2],
-                                f32x16 (&dp)[2], int lane) {
-  const int lq = lane & 31, hh = lane >> 5;
-  bf16x8 ka[D / 16], va[D / 16];
+__device__ inline void sdp_half(const QState<D>& st, const RowReader<D>& rr, uint32_t Kt, uint32_t Vt, int kb,
+                                f32x16 (&s)[2], f32x16 (&dp)[2]) {
 #pragma unroll
   for (int kd = 0; kd < D / 16; ++kd) {
-    ka[kd] = lds_row8<D>(Kt, kb * 32 + lq, kd * 16 + hh * 8);
-    va[kd] = lds_row8<D>(Vt, kb * 32 + lq, kd * 16 + hh * 8);
-  }
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], st.qf[qb][0], f32x16{}, 0, 0, 0);
-    dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], st.of[qb][0], f32x16{}, 0, 0, 0);
-  }
-#pragma unroll
-  for (int kd = 1; kd < D / 16; ++kd)
+    const bf16x8 ka = rr.at(Kt, kb, kd), va = rr.at(Vt, kb, kd);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kd], st.qf[qb][kd], s[qb], 0, 0, 0);
-      dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kd], st.of[qb][kd], dp[qb], 0, 0, 0);
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[qb][kd], kd ? s[qb] : f32x16{}, 0, 0, 0);
+      dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, st.of[qb][kd], kd ? dp[qb] : f32x16{}, 0, 0, 0);
     }
+  }
 }
 
 template <int D>
-__device__ inline void dq_mask(const QState<D>& st, f32x16 (&s)[2], const int32_t* Dt, int32_t kb0, int kh0, bool docs,
+__device__ inline void dq_mask(const QState<D>& st, f32x16 (&s)[2], uint32_t Dt, int32_t kb0, int kh0, bool docs,
                                int hh) {
   asm volatile("; partial tile" ::: "memory");   // keeps the caller's branch real (no if-conversion)
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int kk = kh0 + (r >> 2) * 8 + hh * 4 + (r & 3);
-    const int32_t kd_ = Dt[kk];
+    const int32_t kd_ = lds_ld4i(Dt + 4 * kk);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const bool ok = (kb0 + kk < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
@@ -379,55 +369,49 @@ __device__ inline void ds_half(const QState<D>& st, const f32x16 (&s)[2], const 
 
 // dQ^T[qb][db] += K^T (d rows, 16 keys per step) x dS^T for the half kb
 template <int D>
-__device__ inline void dq_half(QState<D>& st, const char* Kt, int kb, const bf16x8 (&dsf)[2][2], int lane) {
-  const int hh = lane >> 5, s16 = lane & 15, cg = (lane >> 4) & 1;
+__device__ inline void dq_half(QState<D>& st, const TrReader<D>& tr, uint32_t Kt, int kb, const bf16x8 (&dsf)[2][2]) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int k0 = kb * 32 + 16 * t;
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int c0 = db * 32 + 16 * cg;
-      const bf16x8 ka = cat8(lds_tr4<D>(Kt, k0 + 4 * hh, c0, s16), lds_tr4<D>(Kt, k0 + 8 + 4 * hh, c0, s16));
+      const bf16x8 ka = tr.at(Kt, kb * 32 + 16 * t, db);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
         st.acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsf[qb][t], st.acc[qb][db], 0, 0, 0);
     }
-  }
 }
 
 template <int D>
-__device__ inline void dq_tile(QState<D>& st, const char* Kt, const char* Vt, const int32_t* Dt, int32_t kb0,
-                               bool mask, bool docs, float c, int lane) {
+__device__ inline void dq_tile(QState<D>& st, const RowReader<D>& rr, const TrReader<D>& tr, uint32_t Kt,
+                               uint32_t Vt, uint32_t Dt, int32_t kb0, bool mask, bool docs, float c, int lane) {
   const int hh = lane >> 5;
   f32x16 s0[2], dp0[2], s1[2], dp1[2];
   bf16x8 ds0[2][2], ds1[2][2];
-  sdp_half<D>(st, Kt, Vt, 0, s0, dp0, lane);
+  sdp_half<D>(st, rr, Kt, Vt, 0, s0, dp0);
   if (mask) dq_mask<D>(st, s0, Dt, kb0, 0, docs, hh);
   __builtin_amdgcn_sched_barrier(0);
-  sdp_half<D>(st, Kt, Vt, 1, s1, dp1, lane);
+  sdp_half<D>(st, rr, Kt, Vt, 1, s1, dp1);
   ds_half<D>(st, s0, dp0, c, ds0);
   CP_INTERLEAVE(D / 4, 5);
   keep_live(ds0);
   __builtin_amdgcn_sched_barrier(0);
   if (mask) dq_mask<D>(st, s1, Dt, kb0, 32, docs, hh);
   __builtin_amdgcn_sched_barrier(0);
-  dq_half<D>(st, Kt, 0, ds0, lane);
+  dq_half<D>(st, tr, Kt, 0, ds0);
   ds_half<D>(st, s1, dp1, c, ds1);
   CP_INTERLEAVE(D / 8, 9);
   keep_live(ds1);
   __builtin_amdgcn_sched_barrier(0);
-  dq_half<D>(st, Kt, 1, ds1, lane);
+  dq_half<D>(st, tr, Kt, 1, ds1);
 }
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
-  constexpr int TB = BK * D * 2;
-  __shared__ __attribute__((aligned(16))) char kb0_[TB];
-  __shared__ __attribute__((aligned(16))) char kb1_[TB];
-  __shared__ __attribute__((aligned(16))) char vb0_[TB];
-  __shared__ __attribute__((aligned(16))) char vb1_[TB];
-  __shared__ __attribute__((aligned(16))) int32_t xb0_[BK];
-  __shared__ __attribute__((aligned(16))) int32_t xb1_[BK];
+  // LDS arena: K and V tiles and the keys' doc ids, double-buffered.
+  constexpr uint32_t TB = BK * D * 2, RW = BK * 4;
+  constexpr uint32_t K0 = 0, K1 = TB, V0 = 2 * TB, V1 = 3 * TB, X0 = 4 * TB, X1 = X0 + RW;
+  __shared__ __attribute__((aligned(16))) char smem[X1 + RW];
+  const uint32_t S0 = lds_addr(smem);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hh = lane >> 5;
@@ -462,15 +446,15 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
 
   const __bf16* kbase = a.k + (int64_t)kvh * D;
   const __bf16* vbase = a.v + (int64_t)kvh * D;
-  auto issue = [&](int32_t t, char* Kd, char* Vd, int32_t* Xd) {
+  auto issue = [&](int32_t t, uint32_t Kd, uint32_t Vd, uint32_t Xd) {
     tile_load_lds<D, BK, 4>(Kd, kbase, a.kv_stride, t * BK, Lk, wave, lane);
     tile_load_lds<D, BK, 4>(Vd, vbase, a.kv_stride, t * BK, Lk, wave, lane);
     if (docs && wave == 0) {
       const int32_t row = min(t * BK + lane, Lk - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(ks.doc + row), CP_LDS_PTR(Xd), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(ks.doc + row), CP_LDS_AT(Xd), 4, 0, 0);
     }
   };
-  if (kt0 < kt1) issue(kt0, kb0_, vb0_, xb0_);
+  if (kt0 < kt1) issue(kt0, S0 + K0, S0 + V0, S0 + X0);
 
   QState<D> st;
 #pragma unroll
@@ -496,28 +480,31 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
   const int32_t qd_hi = docs ? qs.doc[q1 - 1] : 0;
   const float c = a.scale * LOG2E;
 
+  const RowReader<D> rr(lane);
+  const TrReader<D> tr(lane);
+
   wait_vm0();
   __syncthreads();
 
-  auto step = [&](int32_t t, const char* Kc, const char* Vc, const int32_t* Xc, char* Kn, char* Vn, int32_t* Xn) {
+  auto step = [&](int32_t t, uint32_t Kc, uint32_t Vc, uint32_t Xc, uint32_t Kn, uint32_t Vn, uint32_t Xn) {
     if (t + 1 < kt1) issue(t + 1, Kn, Vn, Xn);
     const int32_t kb0 = t * BK, kb1 = min(Lk, kb0 + BK);
     bool live = wave_live && kb0 < lim_hi;
     bool full = kb1 - kb0 == BK && kb1 <= lim_lo;
     if (docs) {
-      const int32_t kd_lo = Xc[0], kd_hi = Xc[kb1 - kb0 - 1];
+      const int32_t kd_lo = lds_ld4i(Xc), kd_hi = lds_ld4i(Xc + 4 * (kb1 - kb0 - 1));
       live = live && kd_hi >= qd_lo && kd_lo <= qd_hi;
       full = full && qd_lo == qd_hi && kd_lo == kd_hi && kd_lo == qd_lo;
     }
     live = __builtin_amdgcn_readfirstlane((int)live) != 0;   // wave-uniform: scalar branches
     full = __builtin_amdgcn_readfirstlane((int)full) != 0;
-    if (live) dq_tile<D>(st, Kc, Vc, Xc, kb0, !full, docs, c, lane);
+    if (live) dq_tile<D>(st, rr, tr, Kc, Vc, Xc, kb0, !full, docs, c, lane);
     wait_vm0();
     __syncthreads();
   };
   for (int32_t t = kt0; t < kt1; t += 2) {
-    step(t, kb0_, vb0_, xb0_, kb1_, vb1_, xb1_);
-    if (t + 1 < kt1) step(t + 1, kb1_, vb1_, xb1_, kb0_, vb0_, xb0_);
+    step(t, S0 + K0, S0 + V0, S0 + X0, S0 + K1, S0 + V1, S0 + X1);
+    if (t + 1 < kt1) step(t + 1, S0 + K1, S0 + V1, S0 + X1, S0 + K0, S0 + V0, S0 + X0);
   }
 
   if (!wave_live) return;

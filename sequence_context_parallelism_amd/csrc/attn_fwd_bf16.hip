@@ -66,11 +66,10 @@ struct FwdState {
 
 // Scores of a 64-key tile: S^T[kb][qb] = K (keys kb*32..) Q^T (queries qb*32..)
 template <int D>
-__device__ inline void fwd_scores(const FwdState<D>& st, const char* Kt, f32x16 (&s)[2][2], int lane) {
-  const int lq = lane & 31, hh = lane >> 5;
+__device__ inline void fwd_scores(const FwdState<D>& st, const RowReader<D>& rr, uint32_t Kt, f32x16 (&s)[2][2]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const bf16x8 ka = lds_row8<D>(Kt, kb * 32 + lq, hh * 8);
+    const bf16x8 ka = rr.at(Kt, kb, 0);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
       s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[qb][0], f32x16{}, 0, 0, 0);
@@ -79,7 +78,7 @@ __device__ inline void fwd_scores(const FwdState<D>& st, const char* Kt, f32x16 
   for (int kd = 1; kd < D / 16; ++kd) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 ka = lds_row8<D>(Kt, kb * 32 + lq, kd * 16 + hh * 8);
+      const bf16x8 ka = rr.at(Kt, kb, kd);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
         s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[qb][kd], s[kb][qb], 0, 0, 0);
@@ -90,7 +89,7 @@ __device__ inline void fwd_scores(const FwdState<D>& st, const char* Kt, f32x16 
 // Element mask of a partial or ragged tile.  Positions increase along local
 // order, so "key position <= query position" is "key index < lim".
 template <int D>
-__device__ inline void fwd_mask(const FwdState<D>& st, f32x16 (&s)[2][2], const int32_t* Dt, int32_t kb0,
+__device__ inline void fwd_mask(const FwdState<D>& st, f32x16 (&s)[2][2], uint32_t Dt, int32_t kb0,
                                 bool docs, int hh) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -98,7 +97,7 @@ __device__ inline void fwd_mask(const FwdState<D>& st, f32x16 (&s)[2][2], const 
     for (int r = 0; r < 16; ++r) {
       const int kk = kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
       const int32_t kidx = kb0 + kk;
-      const int32_t kd_ = Dt[kk];
+      const int32_t kd_ = lds_ld4i(Dt + 4 * kk);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const bool ok = (kidx < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
@@ -123,9 +122,8 @@ __device__ inline void fwd_tile_max(const f32x16 (&s)[2][2], float (&mx)[2]) {
 // P = exp2(s c - m c), row sums, and O^T += V^T P^T.  Returns this lane's
 // largest tile row-sum share (for the overflow check).
 template <int D>
-__device__ inline float fwd_accumulate(FwdState<D>& st, const char* Vt, const f32x16 (&s)[2][2], float c,
-                                       int lane) {
-  const int hh = lane >> 5, s16 = lane & 15, cg = (lane >> 4) & 1;
+__device__ inline float fwd_accumulate(FwdState<D>& st, const TrReader<D>& tr, uint32_t Vt,
+                                       const f32x16 (&s)[2][2], float c) {
   float tsum[2] = {0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -142,11 +140,9 @@ __device__ inline float fwd_accumulate(FwdState<D>& st, const char* Vt, const f3
         }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int k0 = kb * 32 + 16 * t;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const int c0 = db * 32 + 16 * cg;
-        const bf16x8 va = cat8(lds_tr4<D>(Vt, k0 + 4 * hh, c0, s16), lds_tr4<D>(Vt, k0 + 8 + 4 * hh, c0, s16));
+        const bf16x8 va = tr.at(Vt, kb * 32 + 16 * t, db);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           st.oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][t], st.oacc[qb][db], 0, 0, 0);
@@ -166,11 +162,10 @@ __device__ inline float fwd_accumulate(FwdState<D>& st, const char* Vt, const f3
 // sched_group_barrier because the scheduler would otherwise cluster them.
 
 template <int D>
-__device__ inline void qk_half(const FwdState<D>& st, const char* Kt, int kb, f32x16 (&s)[2], int lane) {
-  const int lq = lane & 31, hh = lane >> 5;
+__device__ inline void qk_half(const FwdState<D>& st, const RowReader<D>& rr, uint32_t Kt, int kb, f32x16 (&s)[2]) {
   bf16x8 ka[D / 16];
 #pragma unroll
-  for (int kd = 0; kd < D / 16; ++kd) ka[kd] = lds_row8<D>(Kt, kb * 32 + lq, kd * 16 + hh * 8);
+  for (int kd = 0; kd < D / 16; ++kd) ka[kd] = rr.at(Kt, kb, kd);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], st.qf[qb][0], f32x16{}, 0, 0, 0);
 #pragma unroll
@@ -195,15 +190,12 @@ __device__ inline void exp_half(const FwdState<D>& st, const f32x16 (&s)[2], bf1
 }
 
 template <int D>
-__device__ inline void pv_half(FwdState<D>& st, const char* Vt, int kb, const bf16x8 (&pf)[2][2], int lane) {
-  const int hh = lane >> 5, s16 = lane & 15, cg = (lane >> 4) & 1;
+__device__ inline void pv_half(FwdState<D>& st, const TrReader<D>& tr, uint32_t Vt, int kb, const bf16x8 (&pf)[2][2]) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int k0 = kb * 32 + 16 * t;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int c0 = db * 32 + 16 * cg;
-      const bf16x8 va = cat8(lds_tr4<D>(Vt, k0 + 4 * hh, c0, s16), lds_tr4<D>(Vt, k0 + 8 + 4 * hh, c0, s16));
+      const bf16x8 va = tr.at(Vt, kb * 32 + 16 * t, db);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
         st.oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][t], st.oacc[qb][db], 0, 0, 0);
@@ -214,13 +206,14 @@ __device__ inline void pv_half(FwdState<D>& st, const char* Vt, int kb, const bf
 
 // Element mask of one 32-key half (keys kh0.. of the tile).
 template <int D>
-__device__ inline void mask_half(const FwdState<D>& st, f32x16 (&s)[2], const int32_t* Dt, int32_t kb0, int kh0,
+__device__ inline void mask_half(const FwdState<D>& st, f32x16 (&s)[2], uint32_t Dt, int32_t kb0, int kh0,
                                  bool docs, int hh) {
+  asm volatile("; partial tile" ::: "memory");   // keeps the caller's branch real (no if-conversion)
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int kk = kh0 + (r >> 2) * 8 + hh * 4 + (r & 3);
     const int32_t kidx = kb0 + kk;
-    const int32_t kd_ = Dt[kk];
+    const int32_t kd_ = lds_ld4i(Dt + 4 * kk);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const bool ok = (kidx < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
@@ -250,17 +243,17 @@ __device__ inline void init_half(FwdState<D>& st, const f32x16 (&s)[2], float c)
 // accumulators throughout): partial tiles insert the mask and tiles with
 // unset reference points insert the init between the pipeline stages.
 template <int D>
-__device__ inline float fwd_tile_piped(FwdState<D>& st, const char* Kt, const char* Vt, const int32_t* Dt,
-                                       int32_t kb0, bool full, bool docs, float c, int lane) {
+__device__ inline float fwd_tile_piped(FwdState<D>& st, const RowReader<D>& rr, const TrReader<D>& tr, uint32_t Kt,
+                                       uint32_t Vt, uint32_t Dt, int32_t kb0, bool full, bool docs, float c, int lane) {
   const int hh = lane >> 5;
   f32x16 s0[2], s1[2];
   bf16x8 p0[2][2], p1[2][2];
   float tsum[2] = {0.f, 0.f};
-  qk_half<D>(st, Kt, 0, s0, lane);
+  qk_half<D>(st, rr, Kt, 0, s0);
   if (!full) mask_half<D>(st, s0, Dt, kb0, 0, docs, hh);
   if (__any((st.mrow[0] == -INFINITY) | (st.mrow[1] == -INFINITY))) init_half<D>(st, s0, c);
   __builtin_amdgcn_sched_barrier(0);
-  qk_half<D>(st, Kt, 1, s1, lane);
+  qk_half<D>(st, rr, Kt, 1, s1);
   exp_half<D>(st, s0, p0, tsum, c);
   CP_INTERLEAVE(D / 8, 7);
   keep_live(p0);   // P0 must be computed here, next to QK1, not sunk past the branches below
@@ -268,11 +261,11 @@ __device__ inline float fwd_tile_piped(FwdState<D>& st, const char* Kt, const ch
   if (!full) mask_half<D>(st, s1, Dt, kb0, 32, docs, hh);
   if (__any((st.mrow[0] == -INFINITY) | (st.mrow[1] == -INFINITY))) init_half<D>(st, s1, c);
   __builtin_amdgcn_sched_barrier(0);
-  pv_half<D>(st, Vt, 0, p0, lane);
+  pv_half<D>(st, tr, Vt, 0, p0);
   exp_half<D>(st, s1, p1, tsum, c);
   CP_INTERLEAVE(D / 8, 7);
   __builtin_amdgcn_sched_barrier(0);
-  pv_half<D>(st, Vt, 1, p1, lane);
+  pv_half<D>(st, tr, Vt, 1, p1);
   st.lrow[0] += tsum[0];
   st.lrow[1] += tsum[1];
   return fmaxf(tsum[0], tsum[1]);
@@ -281,7 +274,7 @@ __device__ inline float fwd_tile_piped(FwdState<D>& st, const char* Kt, const ch
 // Exact online softmax for one tile (the fallback path): running max and
 // rescaling of the accumulators whenever the max rises.
 template <int D>
-__device__ inline void fwd_tile_exact(FwdState<D>& st, const char* Vt, f32x16 (&s)[2][2], float c, int lane) {
+__device__ inline void fwd_tile_exact(FwdState<D>& st, const TrReader<D>& tr, uint32_t Vt, f32x16 (&s)[2][2], float c) {
   float mx[2];
   fwd_tile_max(s, mx);
 #pragma unroll
@@ -296,19 +289,17 @@ __device__ inline void fwd_tile_exact(FwdState<D>& st, const char* Vt, f32x16 (&
       st.moff[qb] = -mn * c;
     }
   }
-  fwd_accumulate<D>(st, Vt, s, c, lane);
+  fwd_accumulate<D>(st, tr, Vt, s, c);
 }
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
-  constexpr int TB = BK * D * 2;     // bytes of one K or V tile
-  __shared__ __attribute__((aligned(16))) char kb0_[TB];
-  __shared__ __attribute__((aligned(16))) char kb1_[TB];
-  __shared__ __attribute__((aligned(16))) char vb0_[TB];
-  __shared__ __attribute__((aligned(16))) char vb1_[TB];
-  __shared__ __attribute__((aligned(16))) int32_t db0_[BK];
-  __shared__ __attribute__((aligned(16))) int32_t db1_[BK];
+  // LDS arena: K and V tiles and the keys' doc ids, double-buffered.
+  constexpr uint32_t TB = BK * D * 2, RW = BK * 4;     // bytes of one K or V tile, of one doc-id row
+  constexpr uint32_t K0 = 0, K1 = TB, V0 = 2 * TB, V1 = 3 * TB, X0 = 4 * TB, X1 = X0 + RW;
+  __shared__ __attribute__((aligned(16))) char smem[X1 + RW];
   __shared__ int32_t overflow_flag;
+  const uint32_t S0 = lds_addr(smem);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hh = lane >> 5;
@@ -344,15 +335,15 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
 
   const __bf16* kbase = a.k + (int64_t)kvh * D;
   const __bf16* vbase = a.v + (int64_t)kvh * D;
-  auto issue = [&](int32_t kt, char* Kd, char* Vd, int32_t* Dd) {
+  auto issue = [&](int32_t kt, uint32_t Kd, uint32_t Vd, uint32_t Dd) {
     tile_load_lds<D, BK, 4>(Kd, kbase, a.kv_stride, kt * BK, Lk, wave, lane);
     tile_load_lds<D, BK, 4>(Vd, vbase, a.kv_stride, kt * BK, Lk, wave, lane);
     if (docs && wave == 0) {
       const int32_t row = min(kt * BK + lane, Lk - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(ks.doc + row), CP_LDS_PTR(Dd), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(ks.doc + row), CP_LDS_AT(Dd), 4, 0, 0);
     }
   };
-  if (kt0 < kt1) issue(kt0, kb0_, vb0_, db0_);
+  if (kt0 < kt1) issue(kt0, S0 + K0, S0 + V0, S0 + X0);
   if (tid == 0) overflow_flag = 0;
 
   // ---- this wave's Q rows as MFMA B operands ----------------------------
@@ -387,12 +378,12 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
   const int32_t qd_lo = docs ? qs.doc[q0 < Lq ? q0 : Lq - 1] : 0;
   const int32_t qd_hi = docs ? qs.doc[q1 - 1] : 0;
 
-  auto classify = [&](int32_t kt, const int32_t* Dc, bool& live, bool& full) {
+  auto classify = [&](int32_t kt, uint32_t Dc, bool& live, bool& full) {
     const int32_t kb0 = kt * BK, kb1 = min(Lk, kb0 + BK);
     live = wave_live && kb0 < lim_hi;
     full = kb1 - kb0 == BK && kb1 <= lim_lo;
     if (docs) {
-      const int32_t kd_lo = Dc[0], kd_hi = Dc[kb1 - kb0 - 1];
+      const int32_t kd_lo = lds_ld4i(Dc), kd_hi = lds_ld4i(Dc + 4 * (kb1 - kb0 - 1));
       live = live && kd_hi >= qd_lo && kd_lo <= qd_hi;
       full = full && qd_lo == qd_hi && kd_lo == kd_hi && kd_lo == qd_lo;
     }
@@ -401,23 +392,25 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
     full = __builtin_amdgcn_readfirstlane((int)full) != 0;
   };
 
+  const RowReader<D> rr(lane);
+  const TrReader<D> tr(lane);
+
   wait_vm0();
   __syncthreads();
 
   // ---- main loop: fixed reference point, accumulators touched by MFMA only --
   float worst = 0.f;   // largest tile row-sum share seen by this lane
-  auto tile = [&](int32_t kt, const char* Kc, const char* Vc, const int32_t* Dc, char* Kn, char* Vn,
-                  int32_t* Dn) {
+  auto tile = [&](int32_t kt, uint32_t Kc, uint32_t Vc, uint32_t Dc, uint32_t Kn, uint32_t Vn, uint32_t Dn) {
     if (kt + 1 < kt1) issue(kt + 1, Kn, Vn, Dn);
     bool live, full;
     classify(kt, Dc, live, full);
-    if (live) worst = fmaxf(worst, fwd_tile_piped<D>(st, Kc, Vc, Dc, kt * BK, full, docs, c, lane));
+    if (live) worst = fmaxf(worst, fwd_tile_piped<D>(st, rr, tr, Kc, Vc, Dc, kt * BK, full, docs, c, lane));
     wait_vm0();
     __syncthreads();
   };
   for (int32_t kt = kt0; kt < kt1; kt += 2) {
-    tile(kt, kb0_, vb0_, db0_, kb1_, vb1_, db1_);
-    if (kt + 1 < kt1) tile(kt + 1, kb1_, vb1_, db1_, kb0_, vb0_, db0_);
+    tile(kt, S0 + K0, S0 + V0, S0 + X0, S0 + K1, S0 + V1, S0 + X1);
+    if (kt + 1 < kt1) tile(kt + 1, S0 + K1, S0 + V1, S0 + X1, S0 + K0, S0 + V0, S0 + X0);
   }
 
   // ---- fallback: a row sum grew past 2^64 -> redo with the exact algorithm --
@@ -426,26 +419,25 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
   if (overflow_flag != 0) {
     asm volatile("; exact fallback" ::: "memory");
     reset();
-    if (kt0 < kt1) issue(kt0, kb0_, vb0_, db0_);
+    if (kt0 < kt1) issue(kt0, S0 + K0, S0 + V0, S0 + X0);
     wait_vm0();
     __syncthreads();
-    auto tile_exact = [&](int32_t kt, const char* Kc, const char* Vc, const int32_t* Dc, char* Kn, char* Vn,
-                          int32_t* Dn) {
+    auto tile_exact = [&](int32_t kt, uint32_t Kc, uint32_t Vc, uint32_t Dc, uint32_t Kn, uint32_t Vn, uint32_t Dn) {
       if (kt + 1 < kt1) issue(kt + 1, Kn, Vn, Dn);
       bool live, full;
       classify(kt, Dc, live, full);
       if (live) {
         f32x16 s[2][2];
-        fwd_scores<D>(st, Kc, s, lane);
+        fwd_scores<D>(st, rr, Kc, s);
         if (!full) fwd_mask<D>(st, s, Dc, kt * BK, docs, hh);
-        fwd_tile_exact<D>(st, Vc, s, c, lane);
+        fwd_tile_exact<D>(st, tr, Vc, s, c);
       }
       wait_vm0();
       __syncthreads();
     };
     for (int32_t kt = kt0; kt < kt1; kt += 2) {
-      tile_exact(kt, kb0_, vb0_, db0_, kb1_, vb1_, db1_);
-      if (kt + 1 < kt1) tile_exact(kt + 1, kb1_, vb1_, db1_, kb0_, vb0_, db0_);
+      tile_exact(kt, S0 + K0, S0 + V0, S0 + X0, S0 + K1, S0 + V1, S0 + X1);
+      if (kt + 1 < kt1) tile_exact(kt + 1, S0 + K1, S0 + V1, S0 + X1, S0 + K0, S0 + V0, S0 + X0);
     }
   }
 

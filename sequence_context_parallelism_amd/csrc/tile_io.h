@@ -34,6 +34,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 #define CP_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+#define CP_LDS_AT(a) ((__attribute__((address_space(3))) void*)(uintptr_t)(a))
 
 template <int D>
 struct Swz {
@@ -77,6 +78,32 @@ __device__ inline void tile_load_lds(char* dst, const __bf16* src, int64_t strid
   }
 }
 
+// The same for a tile at LDS address `dst` (a compile-time offset in the
+// kernel's LDS arena).
+template <int D, int R, int NW>
+__device__ inline void tile_load_lds(uint32_t dst, const __bf16* src, int64_t stride, int32_t row0,
+                                     int32_t valid_rows, int wave, int lane) {
+  constexpr int CHUNKS = D / 8;
+  constexpr int TOTAL = R * CHUNKS;
+  constexpr int PER_WAVE = TOTAL / (64 * NW);
+  static_assert(TOTAL % (64 * NW) == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int slot0 = (wave * PER_WAVE + i) * 64;
+    const int slot = slot0 + lane;
+    const int r = slot / CHUNKS;
+    const int cpos = slot % CHUNKS;
+    int c = cpos;
+    if constexpr (D == 128) c = cpos ^ (((r & 3) << 2) | ((r >> 2) & 3));
+    else c = cpos ^ ((r >> 1) & 7);
+    int32_t row = row0 + r;
+    row = row < valid_rows ? row : valid_rows - 1;
+    const __bf16* g = src + (int64_t)row * stride + c * 8;
+    __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + slot0 * 16),
+                                     16, 0, 0);
+  }
+}
+
 // Row read: 8 consecutive elements (16 bytes) of row r starting at column col
 // (a multiple of 8).
 template <int D>
@@ -100,6 +127,73 @@ __device__ inline bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// ---- reads at 32-bit LDS addresses -----------------------------------------
+// Kernels keep their tiles in one LDS arena and address them with uint32_t
+// LDS addresses, so that a tile's base, a 32-row block and a 16-row step are
+// compile-time constants the compiler folds into the instruction's offset
+// field; only the swizzled lane part lives in VGPRs.  With the swizzle f(r)
+// the lane part of every read is a fixed per-lane value XOR a small constant:
+//   row read of row rb*32 + lq, chunk 2kd + hh:
+//     rb*32*RB + (base ^ (kd << 5)),  base = lq*RB + ((hh ^ f(lq)) << 4)
+//   transposed read of rows R + 8e + 4hh + s/4 (R a multiple of 16), columns
+//   db*32 + 16cg + 4(s%4):
+//     R*RB + (base_e ^ (db << 6))
+// (RB = 2D bytes per row; f depends on r mod 16 only, and the XORed bits
+// never overlap the row part.)
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ inline uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_char*)p; }
+
+__device__ inline bf16x8 lds_ld16(uint32_t a) { return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)a; }
+__device__ inline u32x4 lds_ld16u(uint32_t a) { return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)a; }
+__device__ inline int32_t lds_ld4i(uint32_t a) { return *(const __attribute__((address_space(3))) int32_t*)(uintptr_t)a; }
+
+template <int D>
+__device__ inline int swz_f(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (r >> 1) & 7;
+}
+
+// Row reads (operand with the contraction along d) of a [rows x D] tile.
+template <int D>
+struct RowReader {
+  uint32_t base;
+  __device__ explicit RowReader(int lane) {
+    const int lq = lane & 31, hh = lane >> 5;
+    base = (uint32_t)(lq * 2 * D + ((hh ^ swz_f<D>(lq)) << 4));
+  }
+  // 8 elements of row rb*32 + lq, columns kd*16 + 8hh .. +7
+  __device__ inline bf16x8 at(uint32_t tile, int rb, int kd) const {
+    return lds_ld16(tile + (uint32_t)(rb * 32 * 2 * D) + (base ^ (uint32_t)(kd << 5)));
+  }
+};
+
+// Transposed reads (operand with the contraction along rows): for 16 rows
+// R .. R+15 (R a multiple of 16) and the 32 columns of d block db, lane
+// (s = lane % 16, cg = lane / 16 % 2, hh = lane / 32) receives column
+// db*32 + 16cg + s of rows R + 4hh .. +3 (elements 0..3) and R + 8 + 4hh .. +3
+// (elements 4..7): the A operand of a 32x32x16 MFMA whose K index runs over
+// those 16 rows.
+template <int D>
+struct TrReader {
+  uint32_t b0, b1;
+  __device__ explicit TrReader(int lane) {
+    const int s = lane & 15, cg = (lane >> 4) & 1, hh = lane >> 5;
+    const int c0 = 16 * cg + 4 * (s & 3);
+    const int r0 = 4 * hh + (s >> 2), r1 = 8 + r0;
+    b0 = (uint32_t)(r0 * 2 * D + (((c0 >> 3) ^ swz_f<D>(r0)) << 4) + ((c0 & 4) << 1));
+    b1 = (uint32_t)(r1 * 2 * D + (((c0 >> 3) ^ swz_f<D>(r1)) << 4) + ((c0 & 4) << 1));
+  }
+  __device__ inline bf16x8 at(uint32_t tile, int R, int db) const {
+    const uint32_t t = tile + (uint32_t)(R * 2 * D);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(uintptr_t)(t + (b0 ^ (uint32_t)(db << 6))));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(uintptr_t)(t + (b1 ^ (uint32_t)(db << 6))));
+    return cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
+  }
+};
+
 // ---- instruction-scheduling helpers ----------------------------------------
 // Interleave n MFMAs with v VALU instructions after each (sched_group_barrier
 // masks: 0x008 MFMA, 0x002 VALU).  Used where a stage's MFMAs are independent
@@ -110,6 +204,20 @@ __device__ inline bf16x8 cat8(bf16x4 a, bf16x4 b) {
     _Pragma("unroll") for (int i_ = 0; i_ < (n); ++i_) {      \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      \
       __builtin_amdgcn_sched_group_barrier(0x002, (v), 0);    \
+    }                                                         \
+  } while (0)
+
+// The same with the stage's LDS reads placed too: `lead` reads first, then
+// after each MFMA its v VALU instructions and d more reads (0x100: DS read).
+// Reads are thereby requested a fixed distance ahead of the MFMAs that use
+// them instead of just before.
+#define CP_PIPE(lead, n, v, d)                                \
+  do {                                                        \
+    __builtin_amdgcn_sched_group_barrier(0x100, (lead), 0);   \
+    _Pragma("unroll") for (int i_ = 0; i_ < (n); ++i_) {      \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      \
+      __builtin_amdgcn_sched_group_barrier(0x002, (v), 0);    \
+      __builtin_amdgcn_sched_group_barrier(0x100, (d), 0);    \
     }                                                         \
   } while (0)
 
