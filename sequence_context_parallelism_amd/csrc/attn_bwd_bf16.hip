@@ -180,7 +180,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
   __shared__ __attribute__((aligned(16))) char smem[X1 + RW];
   const uint32_t S0 = lds_addr(smem);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
   const int lq = lane & 31, hh = lane >> 5;
 
   int32_t kvh, kt;                                      // ascending kt = heavy first
@@ -213,11 +214,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
   // Q, dO tiles and the rows' LSE, Delta (and doc ids) of item `it`.  The
   // wave that loaded the LSE (Delta) row converts it in LDS once its loads
   // have landed (prepare): nl = -LSE log2 e, and -Delta.
+  const TileLoader<D, BQ, 4> ldq(a.q_stride * 2, wave, lane), ldo((int64_t)a.hq * D * 2, wave, lane);
   auto issue = [&](int it, uint32_t Qd, uint32_t Od, uint32_t Ld, uint32_t Dd, uint32_t Xd) {
     const int32_t qt = qt1 - 1 - it / G;
     const int head = kvh * G + it % G;
-    tile_load_lds<D, BQ, 4>(Qd, a.q + (int64_t)head * D, a.q_stride, qt * BQ, Lq, wave, lane);
-    tile_load_lds<D, BQ, 4>(Od, a.dout + (int64_t)head * D, (int64_t)a.hq * D, qt * BQ, Lq, wave, lane);
+    if (qt * BQ + BQ <= Lq) {   // whole tile: precomputed lane offsets
+      ldq.load(Qd, (const char*)(a.q + (int64_t)qt * BQ * a.q_stride + (int64_t)head * D));
+      ldo.load(Od, (const char*)(a.dout + ((int64_t)qt * BQ * a.hq + head) * D));
+    } else {                    // ragged last tile: rows clamped
+      tile_load_lds<D, BQ, 4>(Qd, a.q + (int64_t)head * D, a.q_stride, qt * BQ, Lq, wave, lane);
+      tile_load_lds<D, BQ, 4>(Od, a.dout + (int64_t)head * D, (int64_t)a.hq * D, qt * BQ, Lq, wave, lane);
+    }
     const int32_t row = min(qt * BQ + lane, Lq - 1);
     if (wave == 0)
       __builtin_amdgcn_global_load_lds((const void*)(a.lse + (int64_t)head * a.lse_ld + row), CP_LDS_AT(Ld), 4, 0, 0);
@@ -413,7 +420,8 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
   __shared__ __attribute__((aligned(16))) char smem[X1 + RW];
   const uint32_t S0 = lds_addr(smem);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
   const int lq = lane & 31, hh = lane >> 5;
 
   int32_t grp, hidx;
@@ -446,9 +454,16 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
 
   const __bf16* kbase = a.k + (int64_t)kvh * D;
   const __bf16* vbase = a.v + (int64_t)kvh * D;
+  const TileLoader<D, BK, 4> ldr(a.kv_stride * 2, wave, lane);
   auto issue = [&](int32_t t, uint32_t Kd, uint32_t Vd, uint32_t Xd) {
-    tile_load_lds<D, BK, 4>(Kd, kbase, a.kv_stride, t * BK, Lk, wave, lane);
-    tile_load_lds<D, BK, 4>(Vd, vbase, a.kv_stride, t * BK, Lk, wave, lane);
+    if (t * BK + BK <= Lk) {   // whole tile: precomputed lane offsets
+      const int64_t boff = (int64_t)t * BK * a.kv_stride;
+      ldr.load(Kd, (const char*)(kbase + boff));
+      ldr.load(Vd, (const char*)(vbase + boff));
+    } else {                   // ragged last tile: rows clamped
+      tile_load_lds<D, BK, 4>(Kd, kbase, a.kv_stride, t * BK, Lk, wave, lane);
+      tile_load_lds<D, BK, 4>(Vd, vbase, a.kv_stride, t * BK, Lk, wave, lane);
+    }
     if (docs && wave == 0) {
       const int32_t row = min(t * BK + lane, Lk - 1);
       __builtin_amdgcn_global_load_lds((const void*)(ks.doc + row), CP_LDS_AT(Xd), 4, 0, 0);

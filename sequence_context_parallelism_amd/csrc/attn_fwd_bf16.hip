@@ -301,7 +301,8 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
   __shared__ int32_t overflow_flag;
   const uint32_t S0 = lds_addr(smem);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
   const int lq = lane & 31, hh = lane >> 5;
 
   int32_t grp, hidx;
@@ -335,9 +336,16 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
 
   const __bf16* kbase = a.k + (int64_t)kvh * D;
   const __bf16* vbase = a.v + (int64_t)kvh * D;
+  const TileLoader<D, BK, 4> ldr(a.kv_stride * 2, wave, lane);
   auto issue = [&](int32_t kt, uint32_t Kd, uint32_t Vd, uint32_t Dd) {
-    tile_load_lds<D, BK, 4>(Kd, kbase, a.kv_stride, kt * BK, Lk, wave, lane);
-    tile_load_lds<D, BK, 4>(Vd, vbase, a.kv_stride, kt * BK, Lk, wave, lane);
+    if (kt * BK + BK <= Lk) {   // whole tile: precomputed lane offsets
+      const int64_t boff = (int64_t)kt * BK * a.kv_stride;
+      ldr.load(Kd, (const char*)(kbase + boff));
+      ldr.load(Vd, (const char*)(vbase + boff));
+    } else {                     // ragged last tile: rows clamped
+      tile_load_lds<D, BK, 4>(Kd, kbase, a.kv_stride, kt * BK, Lk, wave, lane);
+      tile_load_lds<D, BK, 4>(Vd, vbase, a.kv_stride, kt * BK, Lk, wave, lane);
+    }
     if (docs && wave == 0) {
       const int32_t row = min(kt * BK + lane, Lk - 1);
       __builtin_amdgcn_global_load_lds((const void*)(ks.doc + row), CP_LDS_AT(Dd), 4, 0, 0);

@@ -104,6 +104,38 @@ __device__ inline void tile_load_lds(uint32_t dst, const __bf16* src, int64_t st
   }
 }
 
+// Loads of R x D tiles whose rows are `stride_b` bytes apart, for wave
+// `wave` of NW, with the per-lane byte offsets (row * stride + swizzled
+// chunk) computed once: a tile's loads then cost one 64-bit add each.  Rows
+// must all be valid (row0 + R <= valid rows); the ragged last tile goes
+// through tile_load_lds, which clamps.
+template <int D, int R, int NW>
+struct TileLoader {
+  static constexpr int CHUNKS = D / 8;
+  static constexpr int PER_WAVE = R * CHUNKS / (64 * NW);
+  static_assert(R * CHUNKS % (64 * NW) == 0, "tile must split evenly over the waves");
+  uint32_t off[PER_WAVE];
+  int wave;
+  __device__ TileLoader(int64_t stride_b, int wave_uniform, int lane) : wave(wave_uniform) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int slot = (wave * PER_WAVE + i) * 64 + lane;
+      const int r = slot / CHUNKS, cpos = slot % CHUNKS;
+      int c;
+      if constexpr (D == 128) c = cpos ^ (((r & 3) << 2) | ((r >> 2) & 3));
+      else c = cpos ^ ((r >> 1) & 7);
+      off[i] = (uint32_t)(r * stride_b + c * 16);
+    }
+  }
+  // tile rows start at byte address `src` (wave-uniform); LDS tile at `dst`
+  __device__ inline void load(uint32_t dst, const char* src) const {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src + off[i]),
+                                       CP_LDS_AT(dst + (uint32_t)((wave * PER_WAVE + i) * 1024)), 16, 0, 0);
+  }
+};
+
 // Row read: 8 consecutive elements (16 bytes) of row r starting at column col
 // (a multiple of 8).
 template <int D>
