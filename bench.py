@@ -186,6 +186,30 @@ def kernel_times(wl, cp, torch, iters):
     torch.cuda.synchronize()
     ms = [ev[i].elapsed_time(ev[i + 1]) / iters for i in range(4)]
     rh = wl.rows * wl.hq
+    extra = {}
+    if wl.name == "ulysses_64k":
+        # the all-to-all on either side of the share, emulated: rank 0's query
+        # heads out of the full token-split layer tensor, and its output back
+        layer_hq = wl.hq * wl.group
+        x = torch.empty(wl.S, layer_hq, wl.d, device=wl.dev, dtype=torch.bfloat16)
+        x.normal_()
+        y = torch.empty(wl.S, wl.hq, wl.d, device=wl.dev, dtype=torch.bfloat16)
+        cp.cp_a2a_tokens_to_heads(x, wl.group, 0, y)
+        cp.cp_a2a_heads_to_tokens(y, wl.group, 0, x)
+        ev2 = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        torch.cuda.synchronize()
+        ev2[0].record(st)
+        for _ in range(iters):
+            cp.cp_a2a_tokens_to_heads(x, wl.group, 0, y)
+        ev2[1].record(st)
+        for _ in range(iters):
+            cp.cp_a2a_heads_to_tokens(y, wl.group, 0, x)
+        ev2[2].record(st)
+        torch.cuda.synchronize()
+        moved = 2 * y.numel() * y.element_size()          # read + write of the rank's heads
+        extra["a2a_tokens_to_heads"] = {"ms": ev2[0].elapsed_time(ev2[1]) / iters, "bytes": moved}
+        extra["a2a_heads_to_tokens"] = {"ms": ev2[1].elapsed_time(ev2[2]) / iters, "bytes": moved}
+        del x, y
     # Algorithmic FLOPs per launch (2*d per live pair per Q head per GEMM):
     # the forward's 2 GEMMs; the backward's 5 GEMMs split as dK/dV kernel =
     # S recompute, dP, dV, dK (4) and dQ kernel = dQ (1).  The dQ kernel also
@@ -196,6 +220,7 @@ def kernel_times(wl, cp, torch, iters):
         "dkdv_bf16_kernel": {"ms": ms[1], "flops": 4 * unit, "flops_executed": 4 * unit},
         "dq_bf16_kernel": {"ms": ms[2], "flops": 1 * unit, "flops_executed": 3 * unit},
         "merge_kernel": {"ms": ms[3], "bytes": rh * (3 * wl.d * 4 + 3 * 4)},
+        **extra,
     }
 
 

@@ -217,6 +217,31 @@ cp_status cp_ulysses_share(const cp_shape *sh_full, int64_t S, int32_t sp, int32
                            const void *dout, float *dq, float *dk, float *dv,
                            void *workspace, size_t ws_bytes, void *stream);
 
+/* Emulated Ulysses all-to-all, forward direction ([Ulysses] "현황";
+ * [MaxText] diagram text, A2A): from the token split to the head split.
+ * The sp ranks' token shards are resident together in x [S, h, d] (rank j's
+ * shard is rows [j*S/sp, (j+1)*S/sp); consecutive tokens x_stride elements
+ * apart); rank `rank` receives every token of its heads into y [S, h_out, d]
+ * (contiguous):
+ *   h % sp == 0:  h_out = h/sp,  y[s, i] = x[s, rank*h/sp + i];
+ *   sp % h == 0:  h_out = 1,     y[s, 0] = x[s, rank*h/sp]  (more ranks than
+ *                 heads -- KV heads under GQA: each of the sp/h ranks that
+ *                 share a KV head receives its own copy).
+ * elt_bytes: 2 (bf16) or 4 (fp32).  S must be a multiple of sp; d*elt_bytes
+ * and x_stride*elt_bytes multiples of 16; pointers 16-byte aligned.  A copy
+ * bound by HBM bandwidth.  Errors as for every call (nothing enqueued). */
+cp_status cp_a2a_tokens_to_heads(int64_t S, int32_t h, int32_t d, int32_t elt_bytes, int32_t sp, int32_t rank,
+                                 const void *x, int64_t x_stride, void *y, void *stream);
+
+/* The reverse exchange (the attention output going back to the token split):
+ * rank `rank`'s head-split result o [S, h/sp, d] (contiguous) is written into
+ * the token-split tensor z [S, h, d] (token stride z_stride):
+ *   z[s, rank*h/sp + i] = o[s, i].
+ * Called for every rank it assembles z, whose rows [j*S/sp, ...) are what rank
+ * j holds after the exchange.  h must be a multiple of sp. */
+cp_status cp_a2a_heads_to_tokens(int64_t S, int32_t h, int32_t d, int32_t elt_bytes, int32_t sp, int32_t rank,
+                                 const void *o, void *z, int64_t z_stride, void *stream);
+
 /* Debug dump of the tile classification that drives tile skipping: out
  * [ceil(Lq/bq), ceil(Lk/bk)] int8 (device), 0 = no allowed entry (skipped),
  * 1 = every entry allowed (no element mask), 2 = otherwise.  Entries outside

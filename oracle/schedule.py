@@ -163,3 +163,40 @@ def ulysses_share(q, k, v, sp, rank, *, scale, causal=True, doc=None):
     pos = np.arange(q.shape[0])
     return A.forward(q[:, h0:h1], k[:, g0:g1], v[:, g0:g1], pos, pos,
                      scale=scale, causal=causal, qdoc=doc, kdoc=doc)
+
+
+# ---- the Ulysses all-to-all exchange ---------------------------------------
+# [Ulysses] section 현황 and [MaxText] diagram text (A2A): before attention
+# each rank holds a token shard of every head; the all-to-all gives each rank
+# every token of its own heads; after attention the reverse exchange returns
+# each rank its tokens of every head.  Written as the messages the ranks send
+# each other.
+
+def a2a_heads_of_rank(h, sp, rank):
+    """Heads rank `rank` holds after the forward exchange: its slice of h/sp
+    heads, or -- with more ranks than heads (KV heads under GQA) -- the one
+    head its query heads read, shared with the other sp/h ranks."""
+    if h % sp == 0:
+        return list(range(rank * (h // sp), (rank + 1) * (h // sp)))
+    if sp % h == 0:
+        return [rank * h // sp]
+    raise ValueError(f"h={h} and sp={sp}: one must divide the other")
+
+
+def a2a_tokens_to_heads(shards, rank):
+    """Forward exchange seen by `rank`: rank j sends it the heads of its slice
+    from j's token shard; `rank` stacks the messages in sender order.
+    shards: list of sp arrays [S/sp, h, d]; returns [S, len(heads), d]."""
+    sp = len(shards)
+    heads = a2a_heads_of_rank(shards[0].shape[1], sp, rank)
+    messages = [np.asarray(shards[j])[:, heads, :] for j in range(sp)]
+    return np.concatenate(messages, axis=0)
+
+
+def a2a_heads_to_tokens(outputs, j):
+    """Reverse exchange seen by rank j: rank r sends it j's tokens of r's
+    head-split output; j places them at r's heads.  outputs: list of sp
+    arrays [S, h/sp, d]; returns j's shard [S/sp, h, d]."""
+    sp = len(outputs)
+    n = outputs[0].shape[0] // sp
+    return np.concatenate([np.asarray(outputs[r])[j * n:(j + 1) * n] for r in range(sp)], axis=1)

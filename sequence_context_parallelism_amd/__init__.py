@@ -24,8 +24,8 @@ EXPORTED = (
     "cp_attn_chunk_fwd", "cp_lse_merge", "cp_attn_delta", "cp_attn_chunk_bwd",
     "cp_attn_chunk_bwd_dkdv", "cp_attn_chunk_bwd_dq",
     "cp_zigzag_layout", "cp_ring_schedule", "cp_ring_workspace_bytes", "cp_ring_emulate",
-    "cp_ulysses_workspace_bytes", "cp_ulysses_share", "cp_tile_map", "cp_last_error",
-    "cp_abi_version",
+    "cp_ulysses_workspace_bytes", "cp_ulysses_share", "cp_a2a_tokens_to_heads", "cp_a2a_heads_to_tokens",
+    "cp_tile_map", "cp_last_error", "cp_abi_version",
 )
 
 
@@ -76,6 +76,8 @@ def load(path: str = LIB_PATH):
         "cp_ulysses_workspace_bytes": (SZ, [SH, I64, I32, I32]),
         "cp_ulysses_share": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, P,
                                    SZ, P]),
+        "cp_a2a_tokens_to_heads": (I32, [I64, I32, I32, I32, I32, I32, P, I64, P, P]),
+        "cp_a2a_heads_to_tokens": (I32, [I64, I32, I32, I32, I32, I32, P, P, I64, P]),
         "cp_tile_map": (I32, [SH, cp_span, cp_span, I32, I32, P, P]),
         "cp_last_error": (ctypes.c_char_p, []),
         "cp_abi_version": (I32, []),
@@ -217,6 +219,22 @@ def cp_ulysses_share(shape, S, sp, sp_rank, q, k, v, doc, o, lse, dout=None, dq=
     _check(lib.cp_ulysses_share(ctypes.byref(shape), S, sp, sp_rank, _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(doc), _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                 _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def cp_a2a_tokens_to_heads(x, sp, rank, y, stream=None):
+    """x [S, h, d] (token stride x.stride(0)) -> y [S, h_out, d] for `rank`."""
+    lib = load()
+    S, h, d = x.shape
+    _check(lib.cp_a2a_tokens_to_heads(S, h, d, x.element_size(), sp, rank, _ptr(x), x.stride(0), _ptr(y),
+                                      _stream(stream)))
+
+
+def cp_a2a_heads_to_tokens(o, sp, rank, z, stream=None):
+    """o [S, h/sp, d] of `rank` -> its heads of z [S, h, d] (token stride z.stride(0))."""
+    lib = load()
+    S, h, d = z.shape
+    _check(lib.cp_a2a_heads_to_tokens(S, h, d, z.element_size(), sp, rank, _ptr(o), _ptr(z), z.stride(0),
+                                      _stream(stream)))
 
 
 def cp_tile_map(shape, qs, ks, bq, bk, out, stream=None):

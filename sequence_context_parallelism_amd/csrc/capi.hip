@@ -449,6 +449,48 @@ cp_status cp_ulysses_share(const cp_shape* sh_full, int64_t S, int32_t sp, int32
   return ok();
 }
 
+static cp_status check_a2a(int64_t S, int32_t h, int32_t d, int32_t elt_bytes, int32_t sp, int32_t rank,
+                           const void* a, const void* b, int64_t stride) {
+  if (S <= 0 || S > INT32_MAX) return fail(CP_ERR_ARG, "S=%lld out of range", (long long)S);
+  if (h <= 0 || d <= 0) return fail(CP_ERR_ARG, "h=%d, d=%d must be positive", h, d);
+  if (elt_bytes != 2 && elt_bytes != 4) return fail(CP_ERR_ARG, "elt_bytes=%d not in {2, 4}", elt_bytes);
+  if (sp < 1 || rank < 0 || rank >= sp) return fail(CP_ERR_ARG, "sp=%d, rank=%d", sp, rank);
+  if (S % sp != 0) return fail(CP_ERR_ARG, "S=%lld is not a multiple of sp=%d (equal token shards)", (long long)S, sp);
+  if (h % sp != 0 && sp % h != 0) return fail(CP_ERR_ARG, "h=%d and sp=%d: one must divide the other", h, sp);
+  if (((int64_t)d * elt_bytes) % 16 != 0) return fail(CP_ERR_ALIGN, "a head row (d * elt_bytes) must be a multiple of 16 bytes");
+  if (stride < (int64_t)h * d) return fail(CP_ERR_ARG, "token stride %lld < h*d", (long long)stride);
+  if ((stride * elt_bytes) % 16 != 0) return fail(CP_ERR_ALIGN, "token stride must be a multiple of 16 bytes");
+  CP_TRY(check_ptr(a, "input"));
+  CP_TRY(check_ptr(b, "output"));
+  return ok();
+}
+
+cp_status cp_a2a_tokens_to_heads(int64_t S, int32_t h, int32_t d, int32_t elt_bytes, int32_t sp, int32_t rank,
+                                 const void* x, int64_t x_stride, void* y, void* stream) {
+  CP_TRY(check_a2a(S, h, d, elt_bytes, sp, rank, x, y, x_stride));
+  // heads rank `rank` receives: its slice, or (sp > h) the one KV head its
+  // query heads read, shared with the other sp/h ranks of its group
+  const int32_t h_out = h >= sp ? h / sp : 1;
+  const int32_t h0 = h >= sp ? rank * (h / sp) : (int32_t)((int64_t)rank * h / sp);
+  const int64_t head_b = (int64_t)d * elt_bytes;
+  CP_TRY_HIP(launch_rows_copy(S, (int32_t)(h_out * head_b), (const char*)x + h0 * head_b, x_stride * elt_bytes, y,
+                              h_out * head_b, (hipStream_t)stream),
+             "all-to-all (tokens to heads)");
+  return ok();
+}
+
+cp_status cp_a2a_heads_to_tokens(int64_t S, int32_t h, int32_t d, int32_t elt_bytes, int32_t sp, int32_t rank,
+                                 const void* o, void* z, int64_t z_stride, void* stream) {
+  CP_TRY(check_a2a(S, h, d, elt_bytes, sp, rank, o, z, z_stride));
+  if (h % sp != 0) return fail(CP_ERR_ARG, "h=%d must be a multiple of sp=%d for the output exchange", h, sp);
+  const int32_t h_in = h / sp;
+  const int64_t head_b = (int64_t)d * elt_bytes;
+  CP_TRY_HIP(launch_rows_copy(S, (int32_t)(h_in * head_b), o, h_in * head_b, (char*)z + (int64_t)rank * h_in * head_b,
+                              z_stride * elt_bytes, (hipStream_t)stream),
+             "all-to-all (heads to tokens)");
+  return ok();
+}
+
 cp_status cp_tile_map(const cp_shape* sh, cp_span qs, cp_span ks, int32_t bq, int32_t bk, int8_t* out,
                       void* stream) {
   CP_TRY(check_shape(sh));

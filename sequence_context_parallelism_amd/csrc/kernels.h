@@ -73,6 +73,10 @@ hipError_t launch_delta(int64_t rows, int h, int d, const void* o, int o_f32, co
 hipError_t launch_f32_to_bf16(int64_t n, const float* src, __bf16* dst, hipStream_t stream);
 hipError_t launch_fill_zero(int64_t n, float* dst, hipStream_t stream);
 hipError_t launch_copy_f32(int64_t n, const float* src, float* dst, hipStream_t stream);
+// dst row s = the first row_bytes of src row s (row_bytes and both strides
+// multiples of 16; pointers 16-byte aligned)
+hipError_t launch_rows_copy(int64_t rows, int32_t row_bytes, const void* src, int64_t src_stride_b, void* dst,
+                            int64_t dst_stride_b, hipStream_t stream);
 hipError_t launch_tile_map(SpanD qs, SpanD ks, int causal, int bq, int bk, int8_t* out,
                            hipStream_t stream);
 

@@ -165,3 +165,46 @@ def test_dropped_or_misordered_ring_step_is_caught():
     assert np.max(np.abs(bo - o[rows])) > 1e-3
     go, _ = A.merge(o0, l0, o1, l1)
     assert np.max(np.abs(go - o[rows])) <= 1e-12
+
+
+def test_a2a_golden_and_round_trip():
+    """The all-to-all on labelled integers: element (token, head) carries
+    100*token + head, so every message is checkable by eye; the reverse
+    exchange of the forward result is the identity."""
+    S, h, sp, d = 8, 4, 2, 1
+    full = np.array([[[100 * t + hd] for hd in range(h)] for t in range(S)])
+    shards = [full[j * S // sp:(j + 1) * S // sp] for j in range(sp)]
+    y1 = Z.a2a_tokens_to_heads(shards, 1)
+    assert y1.shape == (S, 2, 1)
+    assert y1[:, :, 0].tolist() == [[100 * t + 2, 100 * t + 3] for t in range(S)]
+    outs = [Z.a2a_tokens_to_heads(shards, r) for r in range(sp)]
+    for j in range(sp):
+        assert np.array_equal(Z.a2a_heads_to_tokens(outs, j), shards[j])
+
+
+def test_a2a_kv_replication_when_ranks_exceed_heads():
+    S, h, sp = 16, 2, 8
+    rng = np.random.default_rng(4)
+    full = rng.standard_normal((S, h, 3))
+    shards = np.split(full, sp)
+    ys = [Z.a2a_tokens_to_heads(shards, r) for r in range(sp)]
+    for r in range(sp):
+        assert ys[r].shape == (S, 1, 3)
+        # the KV head that rank r's query heads read (contiguous GQA groups)
+        hq = 32
+        q_heads = range(r * hq // sp, (r + 1) * hq // sp)
+        kv = {A.kv_head(qh, hq, h) for qh in q_heads}
+        assert kv == {r * h // sp}
+        assert np.array_equal(ys[r][:, 0], full[:, r * h // sp])
+    with pytest.raises(ValueError):
+        Z.a2a_heads_of_rank(3, 2, 0)
+
+
+def test_a2a_result_is_the_ulysses_head_slice():
+    S, hq, hkv, d, sp = 12, 8, 4, 2, 4
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((S, hq, d))
+    qs = np.split(q, sp)
+    for r in range(sp):
+        (a, b), _ = Z.head_slice(hq, hkv, sp, r)
+        assert np.array_equal(Z.a2a_tokens_to_heads(qs, r), q[:, a:b])
