@@ -457,18 +457,40 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
     const int32_t row = q0 + qb * 32 + lq;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (row < Lq) {
-      if (hh == 0) {
-        const float lse = ltot > 0.f ? (st.mrow[qb] * c + __builtin_amdgcn_logf(ltot)) * LN2 : -INFINITY;
-        a.lse[(int64_t)head * a.lse_ld + row] = lse;
+      const float lse = ltot > 0.f ? (st.mrow[qb] * c + __builtin_amdgcn_logf(ltot)) * LN2 : -INFINITY;
+      float* lse_p = a.lse + (int64_t)head * a.lse_ld + row;
+      // merge into a running (O, LSE) (nougat.kr MaxText page, section on
+      // splitting heads or rotating the KV: a step's partial result is merged
+      // into the running one): L = ln(e^La + e^Lb), weights e^(La-L), e^(Lb-L)
+      // in fp64, -inf the identity.
+      float w_acc = 0.f, w_new = 1.f, lse_out = lse;
+      if (a.merge) {
+        const double la = *lse_p, lb = lse;
+        const double m = la > lb ? la : lb;
+        if (m == -INFINITY) {
+          w_new = 0.f;
+        } else {
+          const double L = m + log(exp(la - m) + exp(lb - m));
+          w_acc = (float)exp(la - L);
+          w_new = (float)exp(lb - L);
+          lse_out = (float)L;
+        }
       }
+      if (hh == 0) *lse_p = lse_out;
       const int64_t obase = ((int64_t)row * a.hq + head) * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = db * 32 + j * 8 + hh * 4;
-          const f32x4 v4 = {st.oacc[qb][db][4 * j] * inv, st.oacc[qb][db][4 * j + 1] * inv,
-                            st.oacc[qb][db][4 * j + 2] * inv, st.oacc[qb][db][4 * j + 3] * inv};
+          const float sc = inv * w_new;
+          f32x4 v4 = {st.oacc[qb][db][4 * j] * sc, st.oacc[qb][db][4 * j + 1] * sc,
+                      st.oacc[qb][db][4 * j + 2] * sc, st.oacc[qb][db][4 * j + 3] * sc};
+          if (a.merge) {
+            const f32x4 acc = *(const f32x4*)((const float*)a.o + obase + d);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v4[i] = fmaf(w_acc, acc[i], v4[i]);
+          }
           if (a.o_f32) {
             *(f32x4*)((float*)a.o + obase + d) = v4;
           } else {

@@ -83,9 +83,11 @@ cp_span run_span(int64_t p0, int32_t l0, int64_t p1, int32_t l1, const int32_t* 
 }
 
 // ---- unchecked launchers shared by the entry points and the drivers ----
+// merge: (o fp32, lse) already hold a running result and this chunk's is
+// merged into it in the kernel's epilogue (bf16 inputs only).
 hipError_t run_fwd(const cp_shape* sh, const void* q, const cp_span& qs, const void* k, const void* v,
                    const cp_span& ks, void* o, cp_dtype o_dtype, float* lse, int64_t lse_ld,
-                   hipStream_t st) {
+                   hipStream_t st, bool merge = false) {
   FwdParams p{};
   p.q = (const __bf16*)q; p.k = (const __bf16*)k; p.v = (const __bf16*)v;
   p.qf = (const float*)q; p.kf = (const float*)k; p.vf = (const float*)v;
@@ -94,6 +96,7 @@ hipError_t run_fwd(const cp_shape* sh, const void* q, const cp_span& qs, const v
   p.hq = sh->hq; p.hkv = sh->hkv; p.G = sh->hq / sh->hkv; p.d = sh->d;
   p.scale = sh->scale; p.causal = sh->causal;
   p.o = o; p.o_f32 = o_dtype == CP_F32; p.lse = lse; p.lse_ld = lse_ld;
+  p.merge = merge ? 1 : 0;
   return sh->dtype == CP_F32 ? launch_fwd_f32(p, st) : launch_fwd_bf16(p, st);
 }
 
@@ -361,6 +364,12 @@ cp_status cp_ring_emulate(const cp_shape* sh, int64_t S, int32_t P, int32_t rank
       const char* kj = (const char*)k + (size_t)j * n * sh->kv_stride * in_esz;
       const char* vj = (const char*)v + (size_t)j * n * sh->kv_stride * in_esz;
       const cp_span ks = run_span((int64_t)j * c, c, (int64_t)(2 * P - 1 - j) * c, c, doc ? doc + j * n : nullptr);
+      // bf16 steps after the first merge into the running result in the
+      // forward kernel's epilogue (no partial round trip through HBM)
+      if (s > 0 && !step_o && sh->dtype == CP_BF16) {
+        CP_TRY_HIP(run_fwd(sh, qr, qs, kj, vj, ks, acc_o, CP_F32, lse_r, n, st, true), "ring forward step");
+        continue;
+      }
       float* so = step_o ? step_o + (size_t)s * n * orow : (s == 0 ? acc_o : part_o);
       float* sl = step_lse ? step_lse + (size_t)s * sh->hq * n : (s == 0 ? lse_r : part_lse);
       CP_TRY_HIP(run_fwd(sh, qr, qs, kj, vj, ks, so, CP_F32, sl, n, st), "ring forward step");

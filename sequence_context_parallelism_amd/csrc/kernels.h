@@ -24,6 +24,7 @@ struct FwdParams {
   int o_f32;                 // 1: fp32 O, 0: bf16 O
   float* lse;                // [hq, lse_ld]
   int64_t lse_ld;
+  int merge;                 // 1 (bf16 path, fp32 O): (o, lse) hold a running result; merge into it
   // filled in by the launcher
   int heads_per_wg, qblocks_per_wg, nqt, n_work;
   float scale_log2;
