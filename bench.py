@@ -394,6 +394,18 @@ def main():
                            "traffic": None if traffic is None else round(traffic),
                            "flops_per_launch": kt[dom]["flops"], "ms_per_launch": round(kt[dom]["ms"], 4),
                            "source_sha256_16": kernel_source_hash(dom)}
+    if wl.name == "docs_128k":
+        # rank balance of a ring over these documents (host integer work): the
+        # zigzag layout vs the document-aware two-chunk pairing
+        doc = wl.doc.cpu().numpy()
+        bal = {}
+        for P in (4, 8):
+            w = cp.cp_chunk_work(wl.S, P, doc)
+            zz = np.array([w[r] + w[2 * P - 1 - r] for r in range(P)])
+            _, rw = cp.cp_balanced_pairs(wl.S, P, doc)
+            bal[f"P{P}"] = {"zigzag_max_over_mean": round(float(zz.max() / zz.mean()), 3),
+                            "doc_aware_max_over_mean": round(float(rw.max() / rw.mean()), 3)}
+        out["ring_balance"] = bal
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

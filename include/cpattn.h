@@ -217,6 +217,24 @@ cp_status cp_ulysses_share(const cp_shape *sh_full, int64_t S, int32_t sp, int32
                            const void *dout, float *dq, float *dk, float *dv,
                            void *workspace, size_t ws_bytes, void *stream);
 
+/* Causal work of the 2P chunks of a sequence ([Llama3] "긴 문맥은 어텐션
+ * 비용 이상을 바꾸는 방식": balance ranks by attention compute, not tokens):
+ * work[i] = the number of allowed (query, key) pairs whose query lies in
+ * chunk i (tokens [i*S/(2P), (i+1)*S/(2P))), under the causal mask and, if
+ * doc (HOST array of S int32, non-decreasing, >= 0) is given, the document
+ * mask.  work: HOST array of 2P.  CP_ERR_ARG unless P >= 1 and S > 0 is a
+ * multiple of 2P; CP_ERR_DOCS for ids that are negative or decrease.
+ * Host-only. */
+cp_status cp_chunk_work(int64_t S, int32_t P, const int32_t *doc, int64_t *work);
+
+/* Document-aware alternative to the zigzag layout: assigns the 2P chunks two
+ * per rank so that the largest rank's work (cp_chunk_work) is as small as
+ * possible -- the k-th lightest chunk goes with the k-th heaviest, optimal
+ * for two chunks per rank.  Writes chunks[2r] < chunks[2r+1] (HOST, 2P
+ * entries) and rank_work[r] (HOST, P entries).  With no documents the result
+ * is the zigzag pairing.  Host-only; errors as cp_chunk_work. */
+cp_status cp_balanced_pairs(int64_t S, int32_t P, const int32_t *doc, int32_t *chunks, int64_t *rank_work);
+
 /* Emulated Ulysses all-to-all, forward direction ([Ulysses] "현황";
  * [MaxText] diagram text, A2A): from the token split to the head split.
  * The sp ranks' token shards are resident together in x [S, h, d] (rank j's

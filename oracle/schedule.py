@@ -200,3 +200,45 @@ def a2a_heads_to_tokens(outputs, j):
     sp = len(outputs)
     n = outputs[0].shape[0] // sp
     return np.concatenate([np.asarray(outputs[r])[j * n:(j + 1) * n] for r in range(sp)], axis=1)
+
+
+# ---- balancing ranks by attention work -------------------------------------
+# [Llama3] section 긴 문맥은 어텐션 비용 이상을 바꾸는 방식: with packed documents
+# the ranks must be balanced by the attention each performs, not by tokens.
+
+def chunk_work(S, P, doc=None):
+    """Allowed (query, key) pairs per chunk of S/(2P) queries, counted from
+    the causal (and document) mask itself."""
+    if P < 1 or S <= 0 or S % (2 * P):
+        raise ValueError("need P >= 1 and S > 0 divisible by 2P")
+    c = S // (2 * P)
+    pos = np.arange(S)
+    d = None if doc is None else np.asarray(doc)
+    work = []
+    for i in range(2 * P):
+        rows = pos[i * c:(i + 1) * c]
+        m = A.allowed_mask(rows, pos, True, None if d is None else d[rows], d)
+        work.append(int(m.sum()))
+    return np.array(work, dtype=np.int64)
+
+
+def best_pairing(work):
+    """The two-chunks-per-rank assignment that minimises the largest rank's
+    work, by exhaustive search over all pairings (small P only).  Returns that
+    minimum."""
+    items = list(range(len(work)))
+    best = [None]
+
+    def rec(rest, worst):
+        if best[0] is not None and worst >= best[0]:
+            return
+        if not rest:
+            best[0] = worst
+            return
+        a = rest[0]
+        for k in range(1, len(rest)):
+            b = rest[k]
+            rec(rest[1:k] + rest[k + 1:], max(worst, int(work[a]) + int(work[b])))
+
+    rec(items, 0)
+    return best[0]

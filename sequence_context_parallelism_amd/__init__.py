@@ -24,7 +24,8 @@ EXPORTED = (
     "cp_attn_chunk_fwd", "cp_lse_merge", "cp_attn_delta", "cp_attn_chunk_bwd",
     "cp_attn_chunk_bwd_dkdv", "cp_attn_chunk_bwd_dq",
     "cp_zigzag_layout", "cp_ring_schedule", "cp_ring_workspace_bytes", "cp_ring_emulate",
-    "cp_ulysses_workspace_bytes", "cp_ulysses_share", "cp_a2a_tokens_to_heads", "cp_a2a_heads_to_tokens",
+    "cp_ulysses_workspace_bytes", "cp_ulysses_share", "cp_chunk_work", "cp_balanced_pairs",
+    "cp_a2a_tokens_to_heads", "cp_a2a_heads_to_tokens",
     "cp_tile_map", "cp_last_error", "cp_abi_version",
 )
 
@@ -76,6 +77,8 @@ def load(path: str = LIB_PATH):
         "cp_ulysses_workspace_bytes": (SZ, [SH, I64, I32, I32]),
         "cp_ulysses_share": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, P,
                                    SZ, P]),
+        "cp_chunk_work": (I32, [I64, I32, P, P]),
+        "cp_balanced_pairs": (I32, [I64, I32, P, P, P]),
         "cp_a2a_tokens_to_heads": (I32, [I64, I32, I32, I32, I32, I32, P, I64, P, P]),
         "cp_a2a_heads_to_tokens": (I32, [I64, I32, I32, I32, I32, I32, P, P, I64, P]),
         "cp_tile_map": (I32, [SH, cp_span, cp_span, I32, I32, P, P]),
@@ -219,6 +222,35 @@ def cp_ulysses_share(shape, S, sp, sp_rank, q, k, v, doc, o, lse, dout=None, dq=
     _check(lib.cp_ulysses_share(ctypes.byref(shape), S, sp, sp_rank, _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(doc), _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                 _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def _host_doc(doc):
+    import numpy as np
+    if doc is None:
+        return None, None
+    d = np.ascontiguousarray(doc, dtype=np.int32)
+    return d, d.ctypes.data_as(ctypes.c_void_p)
+
+
+def cp_chunk_work(S, P, doc=None):
+    """Live (query, key) pairs per chunk of S/(2P) tokens; doc: host int32 ids or None."""
+    import numpy as np
+    lib = load()
+    d, dp = _host_doc(doc)
+    w = np.zeros(2 * P, dtype=np.int64)
+    _check(lib.cp_chunk_work(S, P, dp, w.ctypes.data_as(ctypes.c_void_p)))
+    return w
+
+
+def cp_balanced_pairs(S, P, doc=None):
+    """(chunks [P, 2], rank_work [P]) of the document-aware two-chunk layout."""
+    import numpy as np
+    lib = load()
+    d, dp = _host_doc(doc)
+    ch = np.zeros(2 * P, dtype=np.int32)
+    rw = np.zeros(P, dtype=np.int64)
+    _check(lib.cp_balanced_pairs(S, P, dp, ch.ctypes.data_as(ctypes.c_void_p), rw.ctypes.data_as(ctypes.c_void_p)))
+    return ch.reshape(P, 2), rw
 
 
 def cp_a2a_tokens_to_heads(x, sp, rank, y, stream=None):

@@ -4,9 +4,11 @@
 // including scratch, belongs to the caller.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "cpattn.h"
 #include "kernels.h"
@@ -497,6 +499,43 @@ cp_status cp_a2a_heads_to_tokens(int64_t S, int32_t h, int32_t d, int32_t elt_by
   CP_TRY_HIP(launch_rows_copy(S, (int32_t)(h_in * head_b), o, h_in * head_b, (char*)z + (int64_t)rank * h_in * head_b,
                               z_stride * elt_bytes, (hipStream_t)stream),
              "all-to-all (heads to tokens)");
+  return ok();
+}
+
+cp_status cp_chunk_work(int64_t S, int32_t P, const int32_t* doc, int64_t* work) {
+  if (!work) return fail(CP_ERR_ARG, "work is NULL");
+  if (P < 1 || S <= 0 || S % (2 * (int64_t)P) != 0)
+    return fail(CP_ERR_ARG, "need P >= 1 and S > 0 divisible by 2P (S=%lld P=%d)", (long long)S, P);
+  const int64_t c = S / (2 * P);
+  // a query at position i sees the keys of its document up to itself
+  int64_t doc_start = 0;
+  for (int32_t ch = 0; ch < 2 * P; ++ch) work[ch] = 0;
+  for (int64_t i = 0; i < S; ++i) {
+    if (doc) {
+      if (doc[i] < 0 || (i > 0 && doc[i] < doc[i - 1])) return fail(CP_ERR_DOCS, "doc ids must be >= 0 and non-decreasing");
+      if (i > 0 && doc[i] != doc[i - 1]) doc_start = i;
+    }
+    work[i / c] += i - doc_start + 1;
+  }
+  return ok();
+}
+
+cp_status cp_balanced_pairs(int64_t S, int32_t P, const int32_t* doc, int32_t* chunks, int64_t* rank_work) {
+  if (!chunks || !rank_work) return fail(CP_ERR_ARG, "output pointer is NULL");
+  std::vector<int64_t> w(2 * (size_t)(P > 0 ? P : 1));
+  CP_TRY(cp_chunk_work(S, P, doc, w.data()));
+  // two chunks per rank, minimising the largest sum: pair the k-th lightest
+  // chunk with the k-th heaviest (ties broken by position)
+  std::vector<int32_t> order(2 * P);
+  for (int32_t i = 0; i < 2 * P; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return w[x] < w[y]; });
+  for (int32_t r = 0; r < P; ++r) {
+    int32_t a = order[r], b = order[2 * P - 1 - r];
+    if (a > b) std::swap(a, b);
+    chunks[2 * r] = a;
+    chunks[2 * r + 1] = b;
+    rank_work[r] = w[a] + w[b];
+  }
   return ok();
 }
 

@@ -116,3 +116,55 @@ def test_ring_and_ulysses_argument_errors(lib):
                               None, None, None, None, None, 0, None)
     assert st == cp.CP_ERR_ARG                                  # sp=4 does not divide hkv=2
     assert cp.cp_ulysses_workspace_bytes(sh, 1024, 2, True) == 4 * 1024 * 4
+
+
+def _docs(S, seed, median):
+    import cpinputs
+    lens = cpinputs.lognormal_doc_lengths(S, seed=seed, median=median, sigma=1.0, lo=1, hi=S)
+    return cpinputs.doc_ids_from_lengths(lens)
+
+
+@pytest.mark.parametrize("S,P,docs", [(512, 1, False), (512, 2, True), (768, 3, True), (1024, 4, True), (1024, 4, False)])
+def test_chunk_work_matches_mask_count(lib, S, P, docs):
+    doc = _docs(S, 11 + S + P, S // 8) if docs else None
+    got = cp.cp_chunk_work(S, P, doc)
+    assert np.array_equal(got, Z.chunk_work(S, P, doc))
+
+
+@pytest.mark.parametrize("P,seed", [(2, 1), (3, 2), (4, 3), (4, 4), (5, 5)])
+def test_balanced_pairs_are_optimal(lib, P, seed):
+    S = 2 * P * 64
+    doc = _docs(S, seed, 40)
+    pairs, rw = cp.cp_balanced_pairs(S, P, doc)
+    work = Z.chunk_work(S, P, doc)
+    assert sorted(pairs.ravel().tolist()) == list(range(2 * P))          # every chunk exactly once
+    assert np.all(pairs[:, 0] < pairs[:, 1])
+    assert np.array_equal(rw, work[pairs[:, 0]] + work[pairs[:, 1]])
+    assert rw.max() == Z.best_pairing(work)                                # min-max is attained
+
+
+def test_balanced_pairs_without_docs_is_zigzag(lib):
+    S, P = 4096, 8
+    pairs, rw = cp.cp_balanced_pairs(S, P)
+    got = {tuple(p) for p in pairs.tolist()}
+    want = {tuple(int(x) // (S // (2 * P)) for x in (Z.zigzag_layout(S, P, r)[0])) for r in range(P)}
+    assert got == want
+    assert rw.min() == rw.max()          # causal work is exactly balanced by zigzag
+
+
+def test_doc_aware_layout_beats_zigzag_on_packed_documents(lib):
+    import cpinputs
+    S, P = 131072, 8
+    doc = cpinputs.doc_ids_from_lengths(cpinputs.lognormal_doc_lengths(S))
+    work = cp.cp_chunk_work(S, P, doc)
+    zz = np.array([work[r] + work[2 * P - 1 - r] for r in range(P)])
+    _, rw = cp.cp_balanced_pairs(S, P, doc)
+    assert rw.sum() == zz.sum() == work.sum()
+    assert rw.max() <= zz.max()
+
+
+def test_chunk_work_rejects_bad_docs(lib):
+    with pytest.raises(cp.CpError):
+        cp.cp_chunk_work(8, 2, np.array([0, 0, 1, 0, 1, 1, 1, 1], dtype=np.int32))
+    with pytest.raises(cp.CpError):
+        cp.cp_chunk_work(10, 2)
