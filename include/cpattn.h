@@ -217,6 +217,27 @@ cp_status cp_ulysses_share(const cp_shape *sh_full, int64_t S, int32_t sp, int32
                            const void *dout, float *dq, float *dk, float *dv,
                            void *workspace, size_t ws_bytes, void *stream);
 
+/* Workspace bytes cp_allgather_share needs (0 on bad args). */
+size_t cp_allgather_workspace_bytes(const cp_shape *sh, int64_t S, int32_t P, int32_t has_doc, int32_t backward);
+
+/* One rank's share of all-gather context parallelism ([MaxText] diagram text,
+ * All-gather; section "입력을 나눠도 KV가 다시 모이는 이유": causal queries
+ * need every earlier token's KV): the rank keeps its zigzag query shard and
+ * gathers the KV of the whole sequence, so its share is one chunk attention
+ * of its two query runs against all S keys.
+ *   q: the rank's 2c = S/P query rows in local order (chunks rank and
+ *      2P-1-rank; q_stride); k, v: [S, hkv, d] in GLOBAL order (kv_stride);
+ *   doc: NULL or [S] int32 in global order (device).
+ *   Outputs: o [2c, hq, d] (o_dtype), lse [hq, 2c]; with dout [2c, hq, d]
+ *   non-NULL: dq [2c, hq, d] and dk, dv [S, hkv, d] (fp32, written) -- dk, dv
+ *   hold this rank's query rows' contributions (a real job reduce-scatters
+ *   them).  workspace >= cp_allgather_workspace_bytes, 256-byte aligned. */
+cp_status cp_allgather_share(const cp_shape *sh, int64_t S, int32_t P, int32_t rank,
+                             const void *q, const void *k, const void *v, const int32_t *doc,
+                             void *o, cp_dtype o_dtype, float *lse,
+                             const void *dout, float *dq, float *dk, float *dv,
+                             void *workspace, size_t ws_bytes, void *stream);
+
 /* Causal work of the 2P chunks of a sequence ([Llama3] "긴 문맥은 어텐션
  * 비용 이상을 바꾸는 방식": balance ranks by attention compute, not tokens):
  * work[i] = the number of allowed (query, key) pairs whose query lies in

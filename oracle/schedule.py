@@ -242,3 +242,23 @@ def best_pairing(work):
 
     rec(items, 0)
     return best[0]
+
+
+# ---- all-gather share --------------------------------------------------------
+# [MaxText] diagram text, All-gather: a rank keeps its query shard and gathers
+# every key and value, so its share is its queries against the whole sequence.
+
+def allgather_share(q_rank, k, v, S, P, r, *, scale, doc=None, dout=None):
+    """Rank r's share: q_rank holds its rows (zigzag chunks r and 2P-1-r, in
+    local order); k, v the whole sequence in global order.  Returns (o, lse)
+    and, with dout, (dq, dk, dv) where dk, dv are rank r's rows' contributions
+    to every key."""
+    qpos = rank_positions(S, P, r)
+    kpos = np.arange(S)
+    qdoc = None if doc is None else np.asarray(doc)[qpos]
+    o, lse = A.forward(q_rank, k, v, qpos, kpos, scale=scale, causal=True, qdoc=qdoc, kdoc=doc)
+    if dout is None:
+        return o, lse
+    dq, dk, dv = A.backward(q_rank, k, v, dout, lse, A.delta(o, dout), qpos, kpos, scale=scale, causal=True,
+                            qdoc=qdoc, kdoc=doc)
+    return o, lse, dq, dk, dv

@@ -24,7 +24,8 @@ EXPORTED = (
     "cp_attn_chunk_fwd", "cp_lse_merge", "cp_attn_delta", "cp_attn_chunk_bwd",
     "cp_attn_chunk_bwd_dkdv", "cp_attn_chunk_bwd_dq",
     "cp_zigzag_layout", "cp_ring_schedule", "cp_ring_workspace_bytes", "cp_ring_emulate",
-    "cp_ulysses_workspace_bytes", "cp_ulysses_share", "cp_chunk_work", "cp_balanced_pairs",
+    "cp_ulysses_workspace_bytes", "cp_ulysses_share", "cp_allgather_workspace_bytes", "cp_allgather_share",
+    "cp_chunk_work", "cp_balanced_pairs",
     "cp_a2a_tokens_to_heads", "cp_a2a_heads_to_tokens",
     "cp_tile_map", "cp_last_error", "cp_abi_version",
 )
@@ -77,6 +78,8 @@ def load(path: str = LIB_PATH):
         "cp_ulysses_workspace_bytes": (SZ, [SH, I64, I32, I32]),
         "cp_ulysses_share": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, P,
                                    SZ, P]),
+        "cp_allgather_workspace_bytes": (SZ, [SH, I64, I32, I32, I32]),
+        "cp_allgather_share": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, P, SZ, P]),
         "cp_chunk_work": (I32, [I64, I32, P, P]),
         "cp_balanced_pairs": (I32, [I64, I32, P, P, P]),
         "cp_a2a_tokens_to_heads": (I32, [I64, I32, I32, I32, I32, I32, P, I64, P, P]),
@@ -222,6 +225,19 @@ def cp_ulysses_share(shape, S, sp, sp_rank, q, k, v, doc, o, lse, dout=None, dq=
     _check(lib.cp_ulysses_share(ctypes.byref(shape), S, sp, sp_rank, _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(doc), _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                 _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def cp_allgather_workspace_bytes(shape, S, P, has_doc, backward):
+    return load().cp_allgather_workspace_bytes(ctypes.byref(shape), S, P, int(bool(has_doc)), int(bool(backward)))
+
+
+def cp_allgather_share(shape, S, P, rank, q, k, v, doc, o, lse, dout=None, dq=None, dk=None, dv=None,
+                       workspace=None, stream=None):
+    lib = load()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.cp_allgather_share(ctypes.byref(shape), S, P, rank, _ptr(q), _ptr(k), _ptr(v), _ptr(doc),
+                                  _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def _host_doc(doc):

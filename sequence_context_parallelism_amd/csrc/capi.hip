@@ -502,6 +502,65 @@ cp_status cp_a2a_heads_to_tokens(int64_t S, int32_t h, int32_t d, int32_t elt_by
   return ok();
 }
 
+size_t cp_allgather_workspace_bytes(const cp_shape* sh, int64_t S, int32_t P, int32_t has_doc, int32_t backward) {
+  if (check_ring_args(sh, S, P, 0) != CP_OK) return 0;
+  const int64_t n = S / P;
+  return align256((size_t)n * 4 * (has_doc ? 1 : 0)) + (backward ? align256((size_t)n * sh->hq * 4) : 0);
+}
+
+cp_status cp_allgather_share(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, const void* q, const void* k,
+                             const void* v, const int32_t* doc, void* o, cp_dtype o_dtype, float* lse,
+                             const void* dout, float* dq, float* dk, float* dv, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  CP_TRY(check_ring_args(sh, S, P, rank));
+  if (rank < 0) return fail(CP_ERR_ARG, "rank=%d: one rank's share", rank);
+  if (!valid_dtype(o_dtype)) return fail(CP_ERR_ARG, "unknown o_dtype");
+  CP_TRY(check_ptr(q, "q"));
+  CP_TRY(check_ptr(k, "k"));
+  CP_TRY(check_ptr(v, "v"));
+  CP_TRY(check_ptr(o, "o"));
+  if (!lse) return fail(CP_ERR_ARG, "lse is NULL");
+  const bool backward = dout != nullptr;
+  if (backward) {
+    CP_TRY(check_ptr(dout, "dout"));
+    CP_TRY(check_ptr(dq, "dq"));
+    CP_TRY(check_ptr(dk, "dk"));
+    CP_TRY(check_ptr(dv, "dv"));
+  }
+  const size_t need = cp_allgather_workspace_bytes(sh, S, P, doc != nullptr, backward);
+  if (need > 0) {
+    if (!workspace || ws_bytes < need) return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(CP_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t n = S / P;
+  const int32_t c = (int32_t)(S / (2 * P));
+  char* ws = (char*)workspace;
+  // the rank's doc ids in local order (its two zigzag chunks), gathered from
+  // the global array
+  int32_t* qdoc = nullptr;
+  if (doc) {
+    qdoc = (int32_t*)ws;
+    CP_TRY_HIP(hipMemcpyAsync(qdoc, doc + (int64_t)rank * c, (size_t)c * 4, hipMemcpyDeviceToDevice, st), "doc copy");
+    CP_TRY_HIP(hipMemcpyAsync(qdoc + c, doc + (int64_t)(2 * P - 1 - rank) * c, (size_t)c * 4, hipMemcpyDeviceToDevice, st),
+               "doc copy");
+  }
+  float* dlt = (float*)(ws + align256((size_t)n * 4 * (doc ? 1 : 0)));
+  const cp_span qs = run_span((int64_t)rank * c, c, (int64_t)(2 * P - 1 - rank) * c, c, qdoc);
+  const cp_span ks = run_span(0, (int32_t)S, S, 0, doc);
+  CP_TRY_HIP(run_fwd(sh, q, qs, k, v, ks, o, o_dtype, lse, n, st), "all-gather forward");
+  if (backward) {
+    const int64_t orow = (int64_t)sh->hq * sh->d, kvrow = (int64_t)sh->hkv * sh->d;
+    CP_TRY_HIP(launch_fill_zero(n * orow, dq, st), "zero dq");
+    CP_TRY_HIP(launch_fill_zero(S * kvrow, dk, st), "zero dk");
+    CP_TRY_HIP(launch_fill_zero(S * kvrow, dv, st), "zero dv");
+    CP_TRY_HIP(launch_delta(n, sh->hq, sh->d, o, o_dtype == CP_F32, dout, sh->dtype == CP_F32, dlt, n, st),
+               "all-gather delta");
+    CP_TRY_HIP(run_bwd(sh, q, qs, k, v, ks, dout, lse, dlt, n, dq, dk, dv, st), "all-gather backward");
+  }
+  return ok();
+}
+
 cp_status cp_chunk_work(int64_t S, int32_t P, const int32_t* doc, int64_t* work) {
   if (!work) return fail(CP_ERR_ARG, "work is NULL");
   if (P < 1 || S <= 0 || S % (2 * (int64_t)P) != 0)

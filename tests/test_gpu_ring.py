@@ -141,3 +141,37 @@ def test_ulysses_share_is_head_slice(gpu_lib, dtype):
         assert max_abs(host(dq), rdq) <= grad_tol(rdq, tol["grad"])
         assert max_abs(host(dk), rdk) <= grad_tol(rdk, tol["grad"])
         assert max_abs(host(dv), rdv) <= grad_tol(rdv, tol["grad"])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("docs", [False, True], ids=["causal", "docs"])
+def test_allgather_share_one_rank(gpu_lib, dtype, docs):
+    """All-gather share of rank 1 of P=3 (S=768, 8/2 heads, d=128): O, LSE, dQ
+    of its rows and its dK/dV contributions to every key, vs the oracle."""
+    S, P, hq, hkv, d, r = 768, 3, 8, 2, 128, 1
+    (qh, kh, vh, doh), (qd, kd, vd, dod) = inputs(3300 + docs, [(S, hq, d), (S, hkv, d), (S, hkv, d), (S, hq, d)], dtype)
+    doc = None
+    if docs:
+        lens = cpinputs.lognormal_doc_lengths(S, seed=77, median=S // 5, sigma=1.0, lo=8, hi=S)
+        doc = cpinputs.doc_ids_from_lengths(lens)
+    rows = Z.rank_positions(S, P, r)
+    sh = shape_for(hq, hkv, d, dtype)
+    n = S // P
+    q_r = qd[torch.as_tensor(rows, device=DEV)].contiguous()
+    do_r = dod[torch.as_tensor(rows, device=DEV)].contiguous()
+    o = torch.empty(n, hq, d, device=DEV, dtype=dtype)
+    lse = torch.empty(hq, n, device=DEV)
+    dq = torch.empty(n, hq, d, device=DEV)
+    dk = torch.empty(S, hkv, d, device=DEV)
+    dv = torch.empty_like(dk)
+    doc_d = None if doc is None else torch.from_numpy(doc).to(DEV)
+    ws = cp.workspace(cp.cp_allgather_workspace_bytes(sh, S, P, docs, True))
+    cp.cp_allgather_share(sh, S, P, r, q_r, kd, vd, doc_d, o, lse, do_r, dq, dk, dv, workspace=ws)
+    torch.cuda.synchronize()
+    ro, rl, rdq, rdk, rdv = Z.allgather_share(qh[rows], kh, vh, S, P, r, scale=sh.scale, doc=doc, dout=doh[rows])
+    tol = TOL[dtype]
+    assert max_abs(host(o), ro) <= tol["o"]
+    assert lse_err(host(lse), rl) <= tol["lse"]
+    assert max_abs(host(dq), rdq) <= grad_tol(rdq, tol["grad"])
+    assert max_abs(host(dk), rdk) <= grad_tol(rdk, tol["grad"])
+    assert max_abs(host(dv), rdv) <= grad_tol(rdv, tol["grad"])

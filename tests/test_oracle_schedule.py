@@ -208,3 +208,29 @@ def test_a2a_result_is_the_ulysses_head_slice():
     for r in range(sp):
         (a, b), _ = Z.head_slice(hq, hkv, sp, r)
         assert np.array_equal(Z.a2a_tokens_to_heads(qs, r), q[:, a:b])
+
+
+def test_allgather_shares_sum_to_full_attention():
+    """Every rank's all-gather share equals the full attention on its rows, and
+    the ranks' dK/dV contributions sum to the full gradient."""
+    S, P, hq, hkv, d = 48, 3, 4, 2, 3
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((S, hq, d))
+    k = rng.standard_normal((S, hkv, d))
+    v = rng.standard_normal((S, hkv, d))
+    do = rng.standard_normal((S, hq, d))
+    doc = np.repeat(np.arange(4), 12).astype(np.int32)
+    pos = np.arange(S)
+    o, lse = A.forward(q, k, v, pos, pos, scale=0.5, causal=True, qdoc=doc, kdoc=doc)
+    dq, dk, dv = A.backward(q, k, v, do, lse, A.delta(o, do), pos, pos, scale=0.5, causal=True, qdoc=doc, kdoc=doc)
+    dk_sum = np.zeros_like(dk)
+    dv_sum = np.zeros_like(dv)
+    for r in range(P):
+        rows = Z.rank_positions(S, P, r)
+        ro, rl, rdq, rdk, rdv = Z.allgather_share(q[rows], k, v, S, P, r, scale=0.5, doc=doc, dout=do[rows])
+        assert np.max(np.abs(ro - o[rows])) <= 1e-12
+        assert np.max(np.abs(rl - lse[:, rows])) <= 1e-12
+        assert np.max(np.abs(rdq - dq[rows])) <= 1e-12
+        dk_sum += rdk
+        dv_sum += rdv
+    assert np.max(np.abs(dk_sum - dk)) <= 1e-12 and np.max(np.abs(dv_sum - dv)) <= 1e-12
