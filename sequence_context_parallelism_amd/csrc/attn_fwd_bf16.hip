@@ -9,10 +9,13 @@
 // parallelisms).
 //
 // Work decomposition
-//   * one work-group = 4 waves; each wave owns 64 query rows of one query
-//     head.  With grouped-query attention the 4 waves of a group take 4 query
-//     heads that read the same KV head (or 2 heads x 2 row blocks, or 1 head x
-//     4 row blocks), so every K/V tile staged in LDS feeds 4 waves.
+//   * one work-group = 8 waves, two per SIMD; each wave owns 32 query rows of
+//     one query head.  With grouped-query attention the waves take 4 query
+//     heads that read the same KV head x 2 row blocks (or 2 heads x 4, or
+//     1 head x 8), so every K/V tile staged in LDS feeds 8 waves.  Two waves
+//     per SIMD let one wave's softmax VALU work, LDS waits and tile loads run
+//     while the other issues MFMAs (a wave's registers, 256, hold its Q rows,
+//     O accumulators and scores without spilling).
 //   * keys stream through LDS in tiles of 64 rows, double-buffered, copied
 //     with direct-to-LDS loads issued one tile ahead (tile_io.h).
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the K tile is the A operand
@@ -46,7 +49,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int BK = 64;      // keys per tile
-constexpr int QW = 64;      // query rows per wave
+constexpr int NQB = 1;      // 32-row query blocks per wave
+constexpr int QW = 32 * NQB; // query rows per wave
+constexpr int NWV = 8;      // waves per work-group (two per SIMD)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float ROWSUM_LIMIT = 18446744073709551616.0f;   // 2^64
@@ -55,23 +60,23 @@ __device__ inline void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memor
 
 template <int D>
 struct FwdState {
-  bf16x8 qf[2][D / 16];     // B operands: this wave's 64 query rows
-  f32x16 oacc[2][D / 32];   // O^T accumulators [query block][d block]
-  float moff[2];            // -m * c of the lane's query column (0 while unset)
-  float mrow[2];            // m (raw score units); -inf while unset
-  float lrow[2];            // this lane's share of the row sum
-  int32_t lim[2];           // keys [0, lim) are causally visible (and < Lk)
-  int32_t qdoc[2];
+  bf16x8 qf[NQB][D / 16];
+  f32x16 oacc[NQB][D / 32];
+  float moff[NQB];
+  float mrow[NQB];
+  float lrow[NQB];
+  int32_t lim[NQB];
+  int32_t qdoc[NQB];
 };
 
 // Scores of a 64-key tile: S^T[kb][qb] = K (keys kb*32..) Q^T (queries qb*32..)
 template <int D>
-__device__ inline void fwd_scores(const FwdState<D>& st, const RowReader<D>& rr, uint32_t Kt, f32x16 (&s)[2][2]) {
+__device__ inline void fwd_scores(const FwdState<D>& st, const RowReader<D>& rr, uint32_t Kt, f32x16 (&s)[2][NQB]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const bf16x8 ka = rr.at(Kt, kb, 0);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < NQB; ++qb)
       s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[qb][0], f32x16{}, 0, 0, 0);
   }
 #pragma unroll
@@ -80,7 +85,7 @@ __device__ inline void fwd_scores(const FwdState<D>& st, const RowReader<D>& rr,
     for (int kb = 0; kb < 2; ++kb) {
       const bf16x8 ka = rr.at(Kt, kb, kd);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < NQB; ++qb)
         s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[qb][kd], s[kb][qb], 0, 0, 0);
     }
   }
@@ -89,7 +94,7 @@ __device__ inline void fwd_scores(const FwdState<D>& st, const RowReader<D>& rr,
 // Element mask of a partial or ragged tile.  Positions increase along local
 // order, so "key position <= query position" is "key index < lim".
 template <int D>
-__device__ inline void fwd_mask(const FwdState<D>& st, f32x16 (&s)[2][2], uint32_t Dt, int32_t kb0,
+__device__ inline void fwd_mask(const FwdState<D>& st, f32x16 (&s)[2][NQB], uint32_t Dt, int32_t kb0,
                                 bool docs, int hh) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -99,7 +104,7 @@ __device__ inline void fwd_mask(const FwdState<D>& st, f32x16 (&s)[2][2], uint32
       const int32_t kidx = kb0 + kk;
       const int32_t kd_ = lds_ld4i(Dt + 4 * kk);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < NQB; ++qb) {
         const bool ok = (kidx < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
         s[kb][qb][r] = ok ? s[kb][qb][r] : -INFINITY;
       }
@@ -107,9 +112,9 @@ __device__ inline void fwd_mask(const FwdState<D>& st, f32x16 (&s)[2][2], uint32
 }
 
 // Row max of a tile's scores per query column (both lane halves combined).
-__device__ inline void fwd_tile_max(const f32x16 (&s)[2][2], float (&mx)[2]) {
+__device__ inline void fwd_tile_max(const f32x16 (&s)[2][NQB], float (&mx)[NQB]) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     float m0 = fmaxf(s[0][qb][0], s[0][qb][1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) m0 = fmaxf(m0, fmaxf(s[0][qb][r], s[0][qb][r + 1]));
@@ -123,13 +128,13 @@ __device__ inline void fwd_tile_max(const f32x16 (&s)[2][2], float (&mx)[2]) {
 // largest tile row-sum share (for the overflow check).
 template <int D>
 __device__ inline float fwd_accumulate(FwdState<D>& st, const TrReader<D>& tr, uint32_t Vt,
-                                       const f32x16 (&s)[2][2], float c) {
-  float tsum[2] = {0.f, 0.f};
+                                       const f32x16 (&s)[2][NQB], float c) {
+  float tsum[NQB] = {};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    bf16x8 pf[2][2];
+    bf16x8 pf[NQB][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -144,14 +149,15 @@ __device__ inline float fwd_accumulate(FwdState<D>& st, const TrReader<D>& tr, u
       for (int db = 0; db < D / 32; ++db) {
         const bf16x8 va = tr.at(Vt, kb * 32 + 16 * t, db);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < NQB; ++qb)
           st.oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][t], st.oacc[qb][db], 0, 0, 0);
       }
     }
   }
-  st.lrow[0] += tsum[0];
-  st.lrow[1] += tsum[1];
-  return fmaxf(tsum[0], tsum[1]);
+  float mx = 0.f;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) { st.lrow[qb] += tsum[qb]; mx = fmaxf(mx, tsum[qb]); }
+  return mx;
 }
 
 // ---- software-pipelined tile (full tiles, reference point set) -------------
@@ -162,23 +168,23 @@ __device__ inline float fwd_accumulate(FwdState<D>& st, const TrReader<D>& tr, u
 // sched_group_barrier because the scheduler would otherwise cluster them.
 
 template <int D>
-__device__ inline void qk_half(const FwdState<D>& st, const RowReader<D>& rr, uint32_t Kt, int kb, f32x16 (&s)[2]) {
+__device__ inline void qk_half(const FwdState<D>& st, const RowReader<D>& rr, uint32_t Kt, int kb, f32x16 (&s)[NQB]) {
   bf16x8 ka[D / 16];
 #pragma unroll
   for (int kd = 0; kd < D / 16; ++kd) ka[kd] = rr.at(Kt, kb, kd);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], st.qf[qb][0], f32x16{}, 0, 0, 0);
+  for (int qb = 0; qb < NQB; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], st.qf[qb][0], f32x16{}, 0, 0, 0);
 #pragma unroll
   for (int kd = 1; kd < D / 16; ++kd)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kd], st.qf[qb][kd], s[qb], 0, 0, 0);
+    for (int qb = 0; qb < NQB; ++qb) s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kd], st.qf[qb][kd], s[qb], 0, 0, 0);
 }
 
 template <int D>
-__device__ inline void exp_half(const FwdState<D>& st, const f32x16 (&s)[2], bf16x8 (&pf)[2][2], float (&tsum)[2],
+__device__ inline void exp_half(const FwdState<D>& st, const f32x16 (&s)[NQB], bf16x8 (&pf)[NQB][2], float (&tsum)[NQB],
                                 float c) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -190,14 +196,14 @@ __device__ inline void exp_half(const FwdState<D>& st, const f32x16 (&s)[2], bf1
 }
 
 template <int D>
-__device__ inline void pv_half(FwdState<D>& st, const TrReader<D>& tr, uint32_t Vt, int kb, const bf16x8 (&pf)[2][2]) {
+__device__ inline void pv_half(FwdState<D>& st, const TrReader<D>& tr, uint32_t Vt, int kb, const bf16x8 (&pf)[NQB][2]) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const bf16x8 va = tr.at(Vt, kb * 32 + 16 * t, db);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < NQB; ++qb)
         st.oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][t], st.oacc[qb][db], 0, 0, 0);
     }
   }
@@ -206,7 +212,7 @@ __device__ inline void pv_half(FwdState<D>& st, const TrReader<D>& tr, uint32_t 
 
 // Element mask of one 32-key half (keys kh0.. of the tile).
 template <int D>
-__device__ inline void mask_half(const FwdState<D>& st, f32x16 (&s)[2], uint32_t Dt, int32_t kb0, int kh0,
+__device__ inline void mask_half(const FwdState<D>& st, f32x16 (&s)[NQB], uint32_t Dt, int32_t kb0, int kh0,
                                  bool docs, int hh) {
   asm volatile("; partial tile" ::: "memory");   // keeps the caller's branch real (no if-conversion)
 #pragma unroll
@@ -215,7 +221,7 @@ __device__ inline void mask_half(const FwdState<D>& st, f32x16 (&s)[2], uint32_t
     const int32_t kidx = kb0 + kk;
     const int32_t kd_ = lds_ld4i(Dt + 4 * kk);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       const bool ok = (kidx < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
       s[qb][r] = ok ? s[qb][r] : -INFINITY;
     }
@@ -225,9 +231,9 @@ __device__ inline void mask_half(const FwdState<D>& st, f32x16 (&s)[2], uint32_t
 // Rows that have no reference point yet take the max of this half's scores
 // (their accumulators and sums are still zero, so nothing is rescaled).
 template <int D>
-__device__ inline void init_half(FwdState<D>& st, const f32x16 (&s)[2], float c) {
+__device__ inline void init_half(FwdState<D>& st, const f32x16 (&s)[NQB], float c) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     float m0 = fmaxf(s[qb][0], s[qb][1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) m0 = fmaxf(m0, fmaxf(s[qb][r], s[qb][r + 1]));
@@ -239,6 +245,14 @@ __device__ inline void init_half(FwdState<D>& st, const f32x16 (&s)[2], float c)
   }
 }
 
+template <int D>
+__device__ inline bool unset_row(const FwdState<D>& st) {
+  bool u = false;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) u |= st.mrow[qb] == -INFINITY;
+  return u;
+}
+
 // One 64-key tile, one code path for all tiles (the same registers carry the
 // accumulators throughout): partial tiles insert the mask and tiles with
 // unset reference points insert the init between the pipeline stages.
@@ -246,39 +260,36 @@ template <int D>
 __device__ inline float fwd_tile_piped(FwdState<D>& st, const RowReader<D>& rr, const TrReader<D>& tr, uint32_t Kt,
                                        uint32_t Vt, uint32_t Dt, int32_t kb0, bool full, bool docs, float c, int lane) {
   const int hh = lane >> 5;
-  f32x16 s0[2], s1[2];
-  bf16x8 p0[2][2], p1[2][2];
-  float tsum[2] = {0.f, 0.f};
+  f32x16 s0[NQB], s1[NQB];
+  bf16x8 p0[NQB][2], p1[NQB][2];
+  float tsum[NQB] = {};
   qk_half<D>(st, rr, Kt, 0, s0);
   if (!full) mask_half<D>(st, s0, Dt, kb0, 0, docs, hh);
-  if (__any((st.mrow[0] == -INFINITY) | (st.mrow[1] == -INFINITY))) init_half<D>(st, s0, c);
-  __builtin_amdgcn_sched_barrier(0);
+  if (__any(unset_row(st))) init_half<D>(st, s0, c);
   qk_half<D>(st, rr, Kt, 1, s1);
   exp_half<D>(st, s0, p0, tsum, c);
-  CP_INTERLEAVE(D / 8, 7);
+  
   keep_live(p0);   // P0 must be computed here, next to QK1, not sunk past the branches below
-  __builtin_amdgcn_sched_barrier(0);
   if (!full) mask_half<D>(st, s1, Dt, kb0, 32, docs, hh);
-  if (__any((st.mrow[0] == -INFINITY) | (st.mrow[1] == -INFINITY))) init_half<D>(st, s1, c);
-  __builtin_amdgcn_sched_barrier(0);
+  if (__any(unset_row(st))) init_half<D>(st, s1, c);
   pv_half<D>(st, tr, Vt, 0, p0);
   exp_half<D>(st, s1, p1, tsum, c);
-  CP_INTERLEAVE(D / 8, 7);
-  __builtin_amdgcn_sched_barrier(0);
+  
   pv_half<D>(st, tr, Vt, 1, p1);
-  st.lrow[0] += tsum[0];
-  st.lrow[1] += tsum[1];
-  return fmaxf(tsum[0], tsum[1]);
+  float mx = 0.f;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) { st.lrow[qb] += tsum[qb]; mx = fmaxf(mx, tsum[qb]); }
+  return mx;
 }
 
 // Exact online softmax for one tile (the fallback path): running max and
 // rescaling of the accumulators whenever the max rises.
 template <int D>
-__device__ inline void fwd_tile_exact(FwdState<D>& st, const TrReader<D>& tr, uint32_t Vt, f32x16 (&s)[2][2], float c) {
-  float mx[2];
+__device__ inline void fwd_tile_exact(FwdState<D>& st, const TrReader<D>& tr, uint32_t Vt, f32x16 (&s)[2][NQB], float c) {
+  float mx[NQB];
   fwd_tile_max(s, mx);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     const float mn = fmaxf(st.mrow[qb], mx[qb]);
     if (mn > st.mrow[qb]) {
       const float alpha = (st.mrow[qb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((st.mrow[qb] - mn) * c);
@@ -293,7 +304,7 @@ __device__ inline void fwd_tile_exact(FwdState<D>& st, const TrReader<D>& tr, ui
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
+__global__ __launch_bounds__(64 * NWV, 1) void fwd_bf16_kernel(FwdParams a) {
   // LDS arena: K and V tiles and the keys' doc ids, double-buffered.
   constexpr uint32_t TB = BK * D * 2, RW = BK * 4;     // bytes of one K or V tile, of one doc-id row
   constexpr uint32_t K0 = 0, K1 = TB, V0 = 2 * TB, V1 = 3 * TB, X0 = 4 * TB, X1 = X0 + RW;
@@ -336,15 +347,15 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
 
   const __bf16* kbase = a.k + (int64_t)kvh * D;
   const __bf16* vbase = a.v + (int64_t)kvh * D;
-  const TileLoader<D, BK, 4> ldr(a.kv_stride * 2, wave, lane);
+  const TileLoader<D, BK, NWV> ldr(a.kv_stride * 2, wave, lane);
   auto issue = [&](int32_t kt, uint32_t Kd, uint32_t Vd, uint32_t Dd) {
     if (kt * BK + BK <= Lk) {   // whole tile: precomputed lane offsets
       const int64_t boff = (int64_t)kt * BK * a.kv_stride;
       ldr.load(Kd, (const char*)(kbase + boff));
       ldr.load(Vd, (const char*)(vbase + boff));
     } else {                     // ragged last tile: rows clamped
-      tile_load_lds<D, BK, 4>(Kd, kbase, a.kv_stride, kt * BK, Lk, wave, lane);
-      tile_load_lds<D, BK, 4>(Vd, vbase, a.kv_stride, kt * BK, Lk, wave, lane);
+      tile_load_lds<D, BK, NWV>(Kd, kbase, a.kv_stride, kt * BK, Lk, wave, lane);
+      tile_load_lds<D, BK, NWV>(Vd, vbase, a.kv_stride, kt * BK, Lk, wave, lane);
     }
     if (docs && wave == 0) {
       const int32_t row = min(kt * BK + lane, Lk - 1);
@@ -358,7 +369,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
   FwdState<D> st;
   auto reset = [&]() {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) st.oacc[qb][db] = f32x16{};
       st.mrow[qb] = -INFINITY;
@@ -367,7 +378,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
     }
   };
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     const int32_t row = min(q0 + qb * 32 + lq, Lq - 1);
     const bf16x8* src = (const bf16x8*)(a.q + (int64_t)row * a.q_stride + (int64_t)head * D + hh * 8);
 #pragma unroll
@@ -435,7 +446,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
       bool live, full;
       classify(kt, Dc, live, full);
       if (live) {
-        f32x16 s[2][2];
+        f32x16 s[2][NQB];
         fwd_scores<D>(st, rr, Kc, s);
         if (!full) fwd_mask<D>(st, s, Dc, kt * BK, docs, hh);
         fwd_tile_exact<D>(st, tr, Vc, s, c);
@@ -452,7 +463,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(FwdParams a) {
   // ---- epilogue -----------------------------------------------------------
   if (!wave_live) return;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     const float ltot = st.lrow[qb] + __shfl_xor(st.lrow[qb], 32);
     const int32_t row = q0 + qb * 32 + lq;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
@@ -508,7 +519,7 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   FwdParams a = p;
   const int32_t Lq = span_len(a.qs);
   a.heads_per_wg = a.G >= 4 ? 4 : a.G;
-  a.qblocks_per_wg = 4 / a.heads_per_wg;
+  a.qblocks_per_wg = NWV / a.heads_per_wg;
   a.nqt = (Lq + QW * a.qblocks_per_wg - 1) / (QW * a.qblocks_per_wg);
   a.scale_log2 = a.scale * LOG2E;
   const int32_t ngroups = a.hq / a.heads_per_wg;
@@ -516,9 +527,9 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   if (a.n_work == 0) return hipSuccess;
   const int32_t grid = xcd_grid(ngroups, a.nqt);
   if (a.d == 128) {
-    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(grid), dim3(64 * NWV), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(grid), dim3(64 * NWV), 0, stream, a);
   }
   return hipGetLastError();
 }
