@@ -20,13 +20,15 @@
 //     from the accumulator layout straight into the B operand).  4 MFMA
 //     products per (query, key) pair.  The softmax scale of dK is applied once,
 //     at the end.
-//   dq (Q-outer): a work-group owns 64 query rows of 4 query heads sharing a
-//     KV head (like the forward) and streams 64-key tiles of K and V.  Per
-//     tile: S^T = K Q^T, dP^T = V dO^T, P^T, dS^T, dQ^T += K^T dS^T.  3 MFMA
-//     products per pair (S and dP are recomputed rather than exchanged).
-// Both are software-pipelined within a tile: the second half's score MFMAs
+//   dq (Q-outer): a work-group of 8 waves (two per SIMD) owns 64 query rows
+//     of 4 query heads sharing a KV head, 32 rows of one head per wave (like
+//     the forward), and streams 64-key tiles of K and V.  Per tile:
+//     S^T = K Q^T, dP^T = V dO^T, P^T, dS^T, dQ^T += K^T dS^T.  3 MFMA products
+//     per pair (S and dP are recomputed rather than exchanged).
+// dkdv is software-pipelined within a tile: the second half's score MFMAs
 // run beside the first half's exp/dS VALU work, and the first half's gradient
-// MFMAs beside the second half's VALU work (sched_group_barrier).  Masked
+// MFMAs beside the second half's VALU work (sched_group_barrier); in dq the
+// two waves sharing a SIMD overlap each other's VALU and MFMA work.  Masked
 // entries get S = -inf before the exponential, so P = 0; fully masked tiles
 // are skipped and element masks run only on partial or ragged tiles.
 // Heavy-first orders: ascending keys for dkdv, descending queries for dq.
@@ -319,27 +321,31 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
 
 // ================================= dQ =======================================
 
+constexpr int DQB = 1;     // 32-row query blocks per wave (dq)
+constexpr int DQW = 32 * DQB;
+constexpr int DNW = 8;     // waves per work-group (dq), two per SIMD
+
 template <int D>
 struct QState {
-  bf16x8 qf[2][D / 16];     // B operands: 64 query rows
-  bf16x8 of[2][D / 16];     // B operands: their dO rows
-  f32x16 acc[2][D / 32];    // dQ^T accumulators (unscaled) [query block][d block]
-  float nl[2];              // -LSE * log2(e) of the lane's query column
-  float dl[2];              // Delta of the lane's query column
-  int32_t lim[2];           // keys [0, lim) are causally visible (and < Lk)
-  int32_t qdoc[2];
+  bf16x8 qf[DQB][D / 16];   // B operands: the wave's query rows
+  bf16x8 of[DQB][D / 16];   // B operands: their dO rows
+  f32x16 acc[DQB][D / 32];  // dQ^T accumulators (unscaled) [query block][d block]
+  float nl[DQB];            // -LSE * log2(e) of the lane's query column
+  float dl[DQB];            // Delta of the lane's query column
+  int32_t lim[DQB];         // keys [0, lim) are causally visible (and < Lk)
+  int32_t qdoc[DQB];
 };
 
 // S^T and dP^T of the 32-key half kb.  Element r of block qb: query = the
 // lane's column of block qb, key = kb*32 + 8(r/4) + 4hh + r%4.
 template <int D>
 __device__ inline void sdp_half(const QState<D>& st, const RowReader<D>& rr, uint32_t Kt, uint32_t Vt, int kb,
-                                f32x16 (&s)[2], f32x16 (&dp)[2]) {
+                                f32x16 (&s)[DQB], f32x16 (&dp)[DQB]) {
 #pragma unroll
   for (int kd = 0; kd < D / 16; ++kd) {
     const bf16x8 ka = rr.at(Kt, kb, kd), va = rr.at(Vt, kb, kd);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < DQB; ++qb) {
       s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[qb][kd], kd ? s[qb] : f32x16{}, 0, 0, 0);
       dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, st.of[qb][kd], kd ? dp[qb] : f32x16{}, 0, 0, 0);
     }
@@ -347,7 +353,7 @@ __device__ inline void sdp_half(const QState<D>& st, const RowReader<D>& rr, uin
 }
 
 template <int D>
-__device__ inline void dq_mask(const QState<D>& st, f32x16 (&s)[2], uint32_t Dt, int32_t kb0, int kh0, bool docs,
+__device__ inline void dq_mask(const QState<D>& st, f32x16 (&s)[DQB], uint32_t Dt, int32_t kb0, int kh0, bool docs,
                                int hh) {
   asm volatile("; partial tile" ::: "memory");   // keeps the caller's branch real (no if-conversion)
 #pragma unroll
@@ -355,7 +361,7 @@ __device__ inline void dq_mask(const QState<D>& st, f32x16 (&s)[2], uint32_t Dt,
     const int kk = kh0 + (r >> 2) * 8 + hh * 4 + (r & 3);
     const int32_t kd_ = lds_ld4i(Dt + 4 * kk);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < DQB; ++qb) {
       const bool ok = (kb0 + kk < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
       s[qb][r] = ok ? s[qb][r] : -INFINITY;
     }
@@ -363,10 +369,10 @@ __device__ inline void dq_mask(const QState<D>& st, f32x16 (&s)[2], uint32_t Dt,
 }
 
 template <int D>
-__device__ inline void ds_half(const QState<D>& st, const f32x16 (&s)[2], const f32x16 (&dp)[2], float c,
-                               bf16x8 (&dsf)[2][2]) {
+__device__ inline void ds_half(const QState<D>& st, const f32x16 (&s)[DQB], const f32x16 (&dp)[DQB], float c,
+                               bf16x8 (&dsf)[DQB][2]) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < DQB; ++qb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, st.nl[qb]));
@@ -376,14 +382,14 @@ __device__ inline void ds_half(const QState<D>& st, const f32x16 (&s)[2], const 
 
 // dQ^T[qb][db] += K^T (d rows, 16 keys per step) x dS^T for the half kb
 template <int D>
-__device__ inline void dq_half(QState<D>& st, const TrReader<D>& tr, uint32_t Kt, int kb, const bf16x8 (&dsf)[2][2]) {
+__device__ inline void dq_half(QState<D>& st, const TrReader<D>& tr, uint32_t Kt, int kb, const bf16x8 (&dsf)[DQB][2]) {
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const bf16x8 ka = tr.at(Kt, kb * 32 + 16 * t, db);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < DQB; ++qb)
         st.acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsf[qb][t], st.acc[qb][db], 0, 0, 0);
     }
 }
@@ -392,28 +398,22 @@ template <int D>
 __device__ inline void dq_tile(QState<D>& st, const RowReader<D>& rr, const TrReader<D>& tr, uint32_t Kt,
                                uint32_t Vt, uint32_t Dt, int32_t kb0, bool mask, bool docs, float c, int lane) {
   const int hh = lane >> 5;
-  f32x16 s0[2], dp0[2], s1[2], dp1[2];
-  bf16x8 ds0[2][2], ds1[2][2];
+  f32x16 s0[DQB], dp0[DQB], s1[DQB], dp1[DQB];
+  bf16x8 ds0[DQB][2], ds1[DQB][2];
   sdp_half<D>(st, rr, Kt, Vt, 0, s0, dp0);
   if (mask) dq_mask<D>(st, s0, Dt, kb0, 0, docs, hh);
-  __builtin_amdgcn_sched_barrier(0);
   sdp_half<D>(st, rr, Kt, Vt, 1, s1, dp1);
   ds_half<D>(st, s0, dp0, c, ds0);
-  CP_INTERLEAVE(D / 4, 5);
   keep_live(ds0);
-  __builtin_amdgcn_sched_barrier(0);
   if (mask) dq_mask<D>(st, s1, Dt, kb0, 32, docs, hh);
-  __builtin_amdgcn_sched_barrier(0);
   dq_half<D>(st, tr, Kt, 0, ds0);
   ds_half<D>(st, s1, dp1, c, ds1);
-  CP_INTERLEAVE(D / 8, 9);
   keep_live(ds1);
-  __builtin_amdgcn_sched_barrier(0);
   dq_half<D>(st, tr, Kt, 1, ds1);
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
+__global__ __launch_bounds__(64 * DNW, 1) void dq_bf16_kernel(BwdParams a) {
   // LDS arena: K and V tiles and the keys' doc ids, double-buffered.
   constexpr uint32_t TB = BK * D * 2, RW = BK * 4;
   constexpr uint32_t K0 = 0, K1 = TB, V0 = 2 * TB, V1 = 3 * TB, X0 = 4 * TB, X1 = X0 + RW;
@@ -437,11 +437,11 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
   const int32_t Lq = span_len(qs), Lk = span_len(ks);
   const bool causal = a.causal != 0;
   const bool docs = qs.doc != nullptr;
-  const int32_t wg_q0 = qt * BQ * a.qblocks_per_wg;
-  const int32_t wg_q1 = min(Lq, wg_q0 + BQ * a.qblocks_per_wg);
-  const int32_t q0 = wg_q0 + qblk * BQ;
+  const int32_t wg_q0 = qt * DQW * a.qblocks_per_wg;
+  const int32_t wg_q1 = min(Lq, wg_q0 + DQW * a.qblocks_per_wg);
+  const int32_t q0 = wg_q0 + qblk * DQW;
   const bool wave_live = q0 < Lq;
-  const int32_t q1 = min(Lq, q0 + BQ);
+  const int32_t q1 = min(Lq, q0 + DQW);
 
   int32_t klo = 0, khi = Lk;
   if (causal) khi = span_count_le(ks, span_pos(qs, wg_q1 - 1));
@@ -454,15 +454,15 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
 
   const __bf16* kbase = a.k + (int64_t)kvh * D;
   const __bf16* vbase = a.v + (int64_t)kvh * D;
-  const TileLoader<D, BK, 4> ldr(a.kv_stride * 2, wave, lane);
+  const TileLoader<D, BK, DNW> ldr(a.kv_stride * 2, wave, lane);
   auto issue = [&](int32_t t, uint32_t Kd, uint32_t Vd, uint32_t Xd) {
     if (t * BK + BK <= Lk) {   // whole tile: precomputed lane offsets
       const int64_t boff = (int64_t)t * BK * a.kv_stride;
       ldr.load(Kd, (const char*)(kbase + boff));
       ldr.load(Vd, (const char*)(vbase + boff));
     } else {                   // ragged last tile: rows clamped
-      tile_load_lds<D, BK, 4>(Kd, kbase, a.kv_stride, t * BK, Lk, wave, lane);
-      tile_load_lds<D, BK, 4>(Vd, vbase, a.kv_stride, t * BK, Lk, wave, lane);
+      tile_load_lds<D, BK, DNW>(Kd, kbase, a.kv_stride, t * BK, Lk, wave, lane);
+      tile_load_lds<D, BK, DNW>(Vd, vbase, a.kv_stride, t * BK, Lk, wave, lane);
     }
     if (docs && wave == 0) {
       const int32_t row = min(t * BK + lane, Lk - 1);
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
 
   QState<D> st;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < DQB; ++qb) {
     const int32_t row = min(q0 + qb * 32 + lq, Lq - 1);
     const bf16x8* qsrc = (const bf16x8*)(a.q + (int64_t)row * a.q_stride + (int64_t)head * D + hh * 8);
     const bf16x8* osrc = (const bf16x8*)(a.dout + ((int64_t)row * a.hq + head) * D + hh * 8);
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams a) {
 
   if (!wave_live) return;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < DQB; ++qb) {
     const int32_t row = q0 + qb * 32 + lq;
     if (row < Lq) {
       float* dst = a.dq + ((int64_t)row * a.hq + head) * D;
@@ -559,12 +559,12 @@ hipError_t launch_bwd_bf16_dq(const BwdParams& p, hipStream_t stream) {
   if (span_len(p.qs) == 0 || span_len(p.ks) == 0) return hipSuccess;
   BwdParams b = p;
   b.heads_per_wg = b.G >= 4 ? 4 : b.G;
-  b.qblocks_per_wg = 4 / b.heads_per_wg;
-  b.nqt = (span_len(b.qs) + BQ * b.qblocks_per_wg - 1) / (BQ * b.qblocks_per_wg);
+  b.qblocks_per_wg = DNW / b.heads_per_wg;
+  b.nqt = (span_len(b.qs) + DQW * b.qblocks_per_wg - 1) / (DQW * b.qblocks_per_wg);
   b.n_work = b.nqt * (b.hq / b.heads_per_wg);
   const int32_t grid = xcd_grid(b.hq / b.heads_per_wg, b.nqt);
-  if (b.d == 128) hipLaunchKernelGGL(dq_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, b);
-  else hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, b);
+  if (b.d == 128) hipLaunchKernelGGL(dq_bf16_kernel<128>, dim3(grid), dim3(64 * DNW), 0, stream, b);
+  else hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3(grid), dim3(64 * DNW), 0, stream, b);
   return hipGetLastError();
 }
 
