@@ -9,30 +9,30 @@
 // section on long context changing more than the attention cost).
 //
 // Two kernels, neither with atomics (deterministic):
-//   dkdv (KV-outer): a work-group owns 128 keys of one KV head (32 per wave,
-//     their K and V rows held in VGPRs as MFMA B operands and their dK^T,
-//     dV^T accumulators in AGPRs) and streams 64-row tiles of Q and dO for
-//     every query head of the GQA group through LDS (direct-to-LDS loads,
-//     double-buffered).  Per tile: S = Q K^T, dP = dO V^T - Delta (A operands
-//     read row-wise; the dP accumulator starts at -Delta), P = exp2(S c + nl)
-//     with nl = -LSE log2 e, dS = P dP, then dV^T += dO^T P and
-//     dK^T += Q^T dS (A operands read with the LDS transpose read; P and dS go
-//     from the accumulator layout straight into the B operand).  4 MFMA
-//     products per (query, key) pair.  The softmax scale of dK is applied once,
-//     at the end.
+//   dkdv (KV-outer): a work-group of 8 waves (two per SIMD) owns 128 keys of
+//     one KV head and streams 64-row tiles of Q and dO for every query head
+//     of the GQA group through LDS (direct-to-LDS loads, double-buffered).
+//     Wave w takes keys 32(w % 4) .. +31 (their K rows in VGPRs as MFMA B
+//     operands, their V rows resident in LDS, their dK^T and dV^T in
+//     accumulators) against query rows 32(w / 4) .. +31 of each tile.  Per
+//     tile: S = Q K^T, dP = dO V^T - Delta (A operands read row-wise; the dP
+//     accumulator starts at -Delta), P = exp2(S c + nl) with nl = -LSE log2 e,
+//     dS = P dP, then dV^T += dO^T P and dK^T += Q^T dS (A operands read with
+//     the LDS transpose read; P and dS go from the accumulator layout straight
+//     into the B operand).  4 MFMA products per (query, key) pair.  The two
+//     waves of a key block sum their partial dK, dV through LDS at the end;
+//     the softmax scale of dK is applied once, there.
 //   dq (Q-outer): a work-group of 8 waves (two per SIMD) owns 64 query rows
 //     of 4 query heads sharing a KV head, 32 rows of one head per wave (like
 //     the forward), and streams 64-key tiles of K and V.  Per tile:
 //     S^T = K Q^T, dP^T = V dO^T, P^T, dS^T, dQ^T += K^T dS^T.  3 MFMA products
 //     per pair (S and dP are recomputed rather than exchanged).
-// dkdv is software-pipelined within a tile: the second half's score MFMAs
-// run beside the first half's exp/dS VALU work, and the first half's gradient
-// MFMAs beside the second half's VALU work (sched_group_barrier); in dq the
-// two waves sharing a SIMD overlap each other's VALU and MFMA work.  Masked
-// entries get S = -inf before the exponential, so P = 0; fully masked tiles
-// are skipped and element masks run only on partial or ragged tiles.
-// Heavy-first orders: ascending keys for dkdv, descending queries for dq.
-// Inside a dkdv work-group the query tiles run from the last one down.
+// With two waves per SIMD each wave's exp/dS VALU work runs beside the other
+// wave's MFMAs.  Masked entries get S = -inf before the exponential, so P = 0;
+// fully masked tiles are skipped and element masks run only on partial or
+// ragged tiles.  Heavy-first orders: ascending keys for dkdv, descending
+// queries for dq.  Inside a dkdv work-group the query tiles run from the last
+// one down.
 #include "common.h"
 #include "kernels.h"
 #include "tile_io.h"
@@ -64,7 +64,7 @@ __device__ inline float neg_lse2(float lse) { return lse == -INFINITY ? -INFINIT
 
 template <int D>
 struct KvState {
-  bf16x8 kf[D / 16], vf[D / 16];   // this wave's 32 keys as B operands
+  bf16x8 kf[D / 16];               // this wave's 32 keys as B operands (V is read from LDS)
   f32x16 dka[D / 32], dva[D / 32]; // dK^T (unscaled), dV^T accumulators [d block]
   int32_t qlim;                    // queries [qlim, ..) see this lane's key causally
   int32_t kdoc;
@@ -75,7 +75,7 @@ struct KvState {
 // r: key = the lane's key, query row qb*32 + 8(r/4) + 4hh + r%4.
 template <int D>
 __device__ inline void sdp_block(const KvState<D>& st, const RowReader<D>& rr, uint32_t Qt, uint32_t Ot,
-                                 uint32_t NDt, int qb, f32x16& s, f32x16& dp, int lane) {
+                                 uint32_t Vw, uint32_t NDt, int qb, f32x16& s, f32x16& dp, int lane) {
   const int hh = lane >> 5;
   f32x16 init;   // -Delta of the element's query row
 #pragma unroll
@@ -85,11 +85,11 @@ __device__ inline void sdp_block(const KvState<D>& st, const RowReader<D>& rr, u
     for (int i = 0; i < 4; ++i) init[j * 4 + i] = d4[i];
   }
   s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Qt, qb, 0), st.kf[0], f32x16{}, 0, 0, 0);
-  dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Ot, qb, 0), st.vf[0], init, 0, 0, 0);
+  dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Ot, qb, 0), rr.at(Vw, 0, 0), init, 0, 0, 0);
 #pragma unroll
   for (int kd = 1; kd < D / 16; ++kd) {
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Qt, qb, kd), st.kf[kd], s, 0, 0, 0);
-    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Ot, qb, kd), st.vf[kd], dp, 0, 0, 0);
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Ot, qb, kd), rr.at(Vw, 0, kd), dp, 0, 0, 0);
   }
 }
 
@@ -98,9 +98,11 @@ template <int D>
 __device__ inline void dkdv_mask(const KvState<D>& st, f32x16& s, uint32_t QDt, int32_t qa0, int qb,
                                  int32_t Lq, bool docs, int hh) {
   asm volatile("; partial tile" ::: "memory");   // keeps the caller's branch real (no if-conversion)
+  int qbase = qb * 32 + hh * 4;
+  asm volatile("" : "+v"(qbase));   // recomputed here, not hoisted out of the tile loop
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int qr = qb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+    const int qr = qbase + (r >> 2) * 8 + (r & 3);
     const int32_t qidx = qa0 + qr;
     const bool ok = st.kvalid & (qidx < Lq) & (qidx >= st.qlim) & (!docs | (lds_ld4i(QDt + 4 * qr) == st.kdoc));
     s[r] = ok ? s[r] : -INFINITY;
@@ -138,52 +140,85 @@ __device__ inline void dvdk_block(KvState<D>& st, const TrReader<D>& tr, uint32_
   }
 }
 
-// one (64-query tile, head) step for one wave, software-pipelined
+// The wave's 32 keys against the 32-query block qb of the tile (rows
+// 32 qb .. 32 qb + 31): S, dP - Delta, P, dS, then dV^T += dO^T P and
+// dK^T += Q^T dS over query slots 2qb, 2qb + 1.
 template <int D>
-__device__ inline void dkdv_tile(KvState<D>& st, const RowReader<D>& rr, const TrReader<D>& tr, uint32_t Qt,
-                                 uint32_t Ot, uint32_t Nl, uint32_t NDt, uint32_t QDt, int32_t qa0, int32_t Lq,
-                                 bool mask, bool docs, float c, int lane) {
+__device__ inline void dkdv_block(KvState<D>& st, const RowReader<D>& rr, const TrReader<D>& tr, uint32_t Qt,
+                                  uint32_t Ot, uint32_t Vw, uint32_t Nl, uint32_t NDt, uint32_t QDt, int32_t qa0,
+                                  int qb, int32_t Lq, bool mask, bool docs, float c, int lane) {
   const int hh = lane >> 5;
-  f32x16 s0, dp0, s1, dp1;
-  bf16x8 pf0[2], dsf0[2], pf1[2], dsf1[2];
-  // Stage LDS reads: sdp_block = 4 (-Delta) + D/8 row reads for D/8 MFMAs;
-  // pds_block = 4 (nl); dvdk_block = 2 transposed reads per MFMA.
-  sdp_block<D>(st, rr, Qt, Ot, NDt, 0, s0, dp0, lane);
-  CP_PIPE(10, D / 8, 0, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  if (mask) dkdv_mask<D>(st, s0, QDt, qa0, 0, Lq, docs, hh);
-  __builtin_amdgcn_sched_barrier(0);
-  sdp_block<D>(st, rr, Qt, Ot, NDt, 1, s1, dp1, lane);
-  pds_block(s0, dp0, Nl, 0, c, pf0, dsf0, hh);
-  CP_PIPE(14, D / 8, 512 / D, 1);
-  keep_live(pf0);
-  keep_live(dsf0);
-  __builtin_amdgcn_sched_barrier(0);
-  if (mask) dkdv_mask<D>(st, s1, QDt, qa0, 1, Lq, docs, hh);
-  __builtin_amdgcn_sched_barrier(0);
-  dvdk_block<D>(st, tr, Qt, Ot, 0, pf0, dsf0);
-  pds_block(s1, dp1, Nl, 1, c, pf1, dsf1, hh);
-  CP_PIPE(8, D / 8, 512 / D, 2);
-  keep_live(pf1);
-  keep_live(dsf1);
-  __builtin_amdgcn_sched_barrier(0);
-  dvdk_block<D>(st, tr, Qt, Ot, 2, pf1, dsf1);
-  CP_PIPE(4, D / 8, 0, 2);
-  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s, dp;
+  bf16x8 pf[2], dsf[2];
+  sdp_block<D>(st, rr, Qt, Ot, Vw, NDt, qb, s, dp, lane);
+  if (mask) dkdv_mask<D>(st, s, QDt, qa0, qb, Lq, docs, hh);
+  pds_block(s, dp, Nl, qb, c, pf, dsf, hh);
+  dvdk_block<D>(st, tr, Qt, Ot, 2 * qb, pf, dsf);
 }
 
+__device__ inline void lds_st4(uint32_t a, const f32x4& x) {
+  *(__attribute__((address_space(3))) f32x4*)(uintptr_t)a = x;
+}
+
+// Park a 32-key x D accumulator set (accumulator layout) at LDS address P, or
+// add the parked one into it: lane-contiguous 16-byte groups.
 template <int D>
-__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
+__device__ inline void park_acc(uint32_t P, const f32x16 (&acc)[D / 32], int lane) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      lds_st4(P + ((db * 4 + j) * 64 + lane) * 16,
+              f32x4{acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]});
+}
+template <int D>
+__device__ inline void unpark_add(uint32_t P, f32x16 (&acc)[D / 32], int lane) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 x = lds_f4(P + ((db * 4 + j) * 64 + lane) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[db][4 * j + i] += x[i];
+    }
+}
+
+// dst[key row, d] += mul * acc (accumulator layout: d = db*32 + 8j + 4hh + i)
+template <int D>
+__device__ inline void add_rows(float* dst, const f32x16 (&acc)[D / 32], float mul, int hh) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4* p = (f32x4*)(dst + db * 32 + j * 8 + hh * 4);
+      f32x4 o = *p;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] += mul * acc[db][4 * j + i];
+      *p = o;
+    }
+}
+
+constexpr int KNW = 8;   // waves per dkdv work-group: 4 key blocks x 2 query halves
+
+template <int D>
+__global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
   // LDS arena: Q and dO tiles (double-buffered), then per-row LSE (as
-  // -LSE log2 e), -Delta and doc ids, each double-buffered.
+  // -LSE log2 e), -Delta and doc ids, each double-buffered, then the work-
+  // group's V rows (read as MFMA B operands).  After the tile loop the tile
+  // area holds the parked partial accumulators (4 x 32 keys x D floats = as
+  // many bytes as the four tiles).
   constexpr uint32_t TB = BQ * D * 2, RW = BQ * 4;
   constexpr uint32_t Q0 = 0, Q1 = TB, O0 = 2 * TB, O1 = 3 * TB;
   constexpr uint32_t L0 = 4 * TB, L1 = L0 + RW, N0 = L1 + RW, N1 = N0 + RW, X0 = N1 + RW, X1 = X0 + RW;
-  __shared__ __attribute__((aligned(16))) char smem[X1 + RW];
+  constexpr uint32_t VT = X1 + RW;
+  static_assert(4 * BKW * D * 4 <= 4 * TB, "parked accumulators must fit in the tile area");
+  static_assert(VT % 16 == 0, "V tile alignment");
+  __shared__ __attribute__((aligned(16))) char smem[VT + BKG * D * 2];
   const uint32_t S0 = lds_addr(smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
+  const int kb = wave & 3, qh = wave >> 2;                      // key block, query half
   const int lq = lane & 31, hh = lane >> 5;
 
   int32_t kvh, kt;                                      // ascending kt = heavy first
@@ -194,7 +229,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
   const bool causal = a.causal != 0;
   const bool docs = qs.doc != nullptr;
   const int32_t k0 = kt * BKG, k1 = min(Lk, k0 + BKG);
-  const int32_t wk0 = k0 + wave * BKW, wk1 = min(Lk, wk0 + BKW);
+  const int32_t wk0 = k0 + kb * BKW, wk1 = min(Lk, wk0 + BKW);
   const bool wave_has_keys = wk0 < Lk;
 
   // ---- query range of the work-group ------------------------------------
@@ -216,7 +251,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
   // Q, dO tiles and the rows' LSE, Delta (and doc ids) of item `it`.  The
   // wave that loaded the LSE (Delta) row converts it in LDS once its loads
   // have landed (prepare): nl = -LSE log2 e, and -Delta.
-  const TileLoader<D, BQ, 4> ldq(a.q_stride * 2, wave, lane), ldo((int64_t)a.hq * D * 2, wave, lane);
+  const TileLoader<D, BQ, KNW> ldq(a.q_stride * 2, wave, lane), ldo((int64_t)a.hq * D * 2, wave, lane);
   auto issue = [&](int it, uint32_t Qd, uint32_t Od, uint32_t Ld, uint32_t Dd, uint32_t Xd) {
     const int32_t qt = qt1 - 1 - it / G;
     const int head = kvh * G + it % G;
@@ -224,8 +259,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
       ldq.load(Qd, (const char*)(a.q + (int64_t)qt * BQ * a.q_stride + (int64_t)head * D));
       ldo.load(Od, (const char*)(a.dout + ((int64_t)qt * BQ * a.hq + head) * D));
     } else {                    // ragged last tile: rows clamped
-      tile_load_lds<D, BQ, 4>(Qd, a.q + (int64_t)head * D, a.q_stride, qt * BQ, Lq, wave, lane);
-      tile_load_lds<D, BQ, 4>(Od, a.dout + (int64_t)head * D, (int64_t)a.hq * D, qt * BQ, Lq, wave, lane);
+      tile_load_lds<D, BQ, KNW>(Qd, a.q + (int64_t)head * D, a.q_stride, qt * BQ, Lq, wave, lane);
+      tile_load_lds<D, BQ, KNW>(Od, a.dout + (int64_t)head * D, (int64_t)a.hq * D, qt * BQ, Lq, wave, lane);
     }
     const int32_t row = min(qt * BQ + lane, Lq - 1);
     if (wave == 0)
@@ -239,18 +274,24 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
     if (wave == 0) lds_stf(Ld + 4 * lane, neg_lse2(lds_ldf(Ld + 4 * lane)));
     else if (wave == 1) lds_stf(Dd + 4 * lane, -lds_ldf(Dd + 4 * lane));
   };
-  if (nitems > 0) issue(0, S0 + Q0, S0 + O0, S0 + L0, S0 + N0, S0 + X0);
+  if (nitems > 0) {
+    // the work-group's V rows (rows past Lk clamped: their keys are masked)
+    if (k0 + BKG <= Lk) {
+      const TileLoader<D, BKG, KNW> ldv(a.kv_stride * 2, wave, lane);
+      ldv.load(S0 + VT, (const char*)(a.v + (int64_t)k0 * a.kv_stride + (int64_t)kvh * D));
+    } else {
+      tile_load_lds<D, BKG, KNW>(S0 + VT, a.v + (int64_t)kvh * D, a.kv_stride, k0, Lk, wave, lane);
+    }
+    issue(0, S0 + Q0, S0 + O0, S0 + L0, S0 + N0, S0 + X0);
+  }
+  const uint32_t Vw = S0 + VT + kb * (BKW * D * 2);   // this wave's 32 V rows
 
   KvState<D> st;
   {
     const int32_t mykey = min(wk0 + lq, Lk - 1);
     const bf16x8* ksrc = (const bf16x8*)(a.k + (int64_t)mykey * a.kv_stride + (int64_t)kvh * D + hh * 8);
-    const bf16x8* vsrc = (const bf16x8*)(a.v + (int64_t)mykey * a.kv_stride + (int64_t)kvh * D + hh * 8);
 #pragma unroll
-    for (int kd = 0; kd < D / 16; ++kd) {
-      st.kf[kd] = ksrc[kd * 2];
-      st.vf[kd] = vsrc[kd * 2];
-    }
+    for (int kd = 0; kd < D / 16; ++kd) st.kf[kd] = ksrc[kd * 2];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) { st.dka[db] = f32x16{}; st.dva[db] = f32x16{}; }
     st.qlim = causal ? span_count_lt(qs, span_pos(ks, mykey)) : 0;
@@ -276,17 +317,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
   auto step = [&](int it, uint32_t Qc, uint32_t Oc, uint32_t Lc, uint32_t Dc, uint32_t Xc, uint32_t Qn,
                   uint32_t On, uint32_t Ln, uint32_t Dn, uint32_t Xn) {
     if (it + 1 < nitems) issue(it + 1, Qn, On, Ln, Dn, Xn);
-    const int32_t qa0 = (qt1 - 1 - it / G) * BQ, qa1 = min(Lq, qa0 + BQ);
-    bool live = wave_has_keys && qa1 - 1 >= q_none;
-    bool full = qa1 - qa0 == BQ && qa0 >= q_all && wk1 - wk0 == BKW;
-    if (docs) {
-      const int32_t qd_lo = lds_ld4i(Xc), qd_hi = lds_ld4i(Xc + 4 * (qa1 - qa0 - 1));
+    const int32_t qa0 = (qt1 - 1 - it / G) * BQ;
+    const int32_t wq0 = qa0 + 32 * qh, wq1 = min(Lq, wq0 + 32);   // this wave's query rows
+    bool live = wave_has_keys && wq0 < Lq && wq1 - 1 >= q_none;
+    bool full = wq1 - wq0 == 32 && wq0 >= q_all && wk1 - wk0 == BKW;
+    if (docs) {   // both reads stay inside the 64-row buffer (qa0 < Lq)
+      const int32_t qd_lo = lds_ld4i(Xc + 4 * min(32 * qh, Lq - 1 - qa0)), qd_hi = lds_ld4i(Xc + 4 * (wq1 - 1 - qa0));
       live = live && kd_hi >= qd_lo && kd_lo <= qd_hi;
       full = full && qd_lo == qd_hi && kd_lo == kd_hi && kd_lo == qd_lo;
     }
     live = __builtin_amdgcn_readfirstlane((int)live) != 0;   // wave-uniform: scalar branches
     full = __builtin_amdgcn_readfirstlane((int)full) != 0;
-    if (live) dkdv_tile<D>(st, rr, tr, Qc, Oc, Lc, Dc, Xc, qa0, Lq, !full, docs, c, lane);
+    if (live) dkdv_block<D>(st, rr, tr, Qc, Oc, Vw, Lc, Dc, Xc, qa0, qh, Lq, !full, docs, c, lane);
     wait_vm0();
     if (it + 1 < nitems) prepare(Ln, Dn);
     __syncthreads();
@@ -297,25 +339,26 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams a) {
       step(it + 1, S0 + Q1, S0 + O1, S0 + L1, S0 + N1, S0 + X1, S0 + Q0, S0 + O0, S0 + L0, S0 + N0, S0 + X0);
   }
 
-  // ---- dK (scaled here), dV: exclusive to this work-group, read-modify-write --
-  if (st.kvalid && wave_has_keys) {
-    const int64_t base = ((int64_t)(wk0 + lq) * a.hkv + kvh) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = db * 32 + j * 8 + hh * 4;
-        f32x4* pk = (f32x4*)(a.dk + base + d);
-        f32x4* pv = (f32x4*)(a.dv + base + d);
-        f32x4 ok = *pk, ov = *pv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ok[i] += a.scale * st.dka[db][4 * j + i];
-          ov[i] += st.dva[db][4 * j + i];
-        }
-        *pk = ok;
-        *pv = ov;
-      }
+  // ---- sum the two query halves; dK (scaled here), dV: exclusive to this
+  // work-group, read-modify-write.  The second-half wave of key block kb
+  // parks its dK^T, the first-half wave adds it and writes dK; then the
+  // roles swap for dV.  The loop ended with a barrier: the arena is free.
+  const uint32_t P = S0 + kb * (BKW * D * 4);
+  const bool writer = st.kvalid && wave_has_keys;
+  float* const krow = a.dk + ((int64_t)(wk0 + lq) * a.hkv + kvh) * D;
+  float* const vrow = a.dv + ((int64_t)(wk0 + lq) * a.hkv + kvh) * D;
+  if (qh == 1) park_acc<D>(P, st.dka, lane);
+  __syncthreads();
+  if (qh == 0) {
+    unpark_add<D>(P, st.dka, lane);
+    if (writer) add_rows<D>(krow, st.dka, a.scale, hh);
+  }
+  __syncthreads();
+  if (qh == 0) park_acc<D>(P, st.dva, lane);
+  __syncthreads();
+  if (qh == 1) {
+    unpark_add<D>(P, st.dva, lane);
+    if (writer) add_rows<D>(vrow, st.dva, 1.0f, hh);
   }
 }
 
@@ -550,8 +593,8 @@ hipError_t launch_bwd_bf16_dkdv(const BwdParams& p, hipStream_t stream) {
   a.nkt = (span_len(a.ks) + BKG - 1) / BKG;
   a.n_work = a.nkt * a.hkv;
   const int32_t grid = xcd_grid(a.hkv, a.nkt);
-  if (a.d == 128) hipLaunchKernelGGL(dkdv_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(dkdv_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, a);
+  if (a.d == 128) hipLaunchKernelGGL(dkdv_bf16_kernel<128>, dim3(grid), dim3(64 * KNW), 0, stream, a);
+  else hipLaunchKernelGGL(dkdv_bf16_kernel<64>, dim3(grid), dim3(64 * KNW), 0, stream, a);
   return hipGetLastError();
 }
 
