@@ -72,10 +72,12 @@ struct KvState {
 };
 
 // S and dP - Delta of the 32-query block qb of the tile.  Accumulator element
-// r: key = the lane's key, query row qb*32 + 8(r/4) + 4hh + r%4.
+// r: key = the lane's key, query row qb*32 + 8(r/4) + 4hh + r%4.  rq reads
+// rows of block qb (its base holds the block offset); vb is the lane's
+// address in the wave's V rows.
 template <int D>
-__device__ inline void sdp_block(const KvState<D>& st, const RowReader<D>& rr, uint32_t Qt, uint32_t Ot,
-                                 uint32_t Vw, uint32_t NDt, int qb, f32x16& s, f32x16& dp, int lane) {
+__device__ inline void sdp_block(const KvState<D>& st, const RowReader<D>& rq, uint32_t Qt, uint32_t Ot,
+                                 uint32_t vb, uint32_t NDt, int qb, f32x16& s, f32x16& dp, int lane) {
   const int hh = lane >> 5;
   f32x16 init;   // -Delta of the element's query row
 #pragma unroll
@@ -84,12 +86,13 @@ __device__ inline void sdp_block(const KvState<D>& st, const RowReader<D>& rr, u
 #pragma unroll
     for (int i = 0; i < 4; ++i) init[j * 4 + i] = d4[i];
   }
-  s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Qt, qb, 0), st.kf[0], f32x16{}, 0, 0, 0);
-  dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Ot, qb, 0), rr.at(Vw, 0, 0), init, 0, 0, 0);
+  s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq.at(Qt, 0, 0), st.kf[0], f32x16{}, 0, 0, 0);
+  dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq.at(Ot, 0, 0), lds_ld16(vb), init, 0, 0, 0);
 #pragma unroll
   for (int kd = 1; kd < D / 16; ++kd) {
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Qt, qb, kd), st.kf[kd], s, 0, 0, 0);
-    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rr.at(Ot, qb, kd), rr.at(Vw, 0, kd), dp, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq.at(Qt, 0, kd), st.kf[kd], s, 0, 0, 0);
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq.at(Ot, 0, kd), lds_ld16(vb ^ (uint32_t)(kd << 5)), dp, 0,
+                                                 0, 0);
   }
 }
 
@@ -125,7 +128,8 @@ __device__ inline void pds_block(const f32x16& s, const f32x16& dp, uint32_t Nl,
   }
 }
 
-// dV^T += dO^T P, dK^T += Q^T dS over the query slots t0, t0 + 1.
+// dV^T += dO^T P, dK^T += Q^T dS over the query slots t0, t0 + 1 (slots
+// counted from the row offset held in tr's bases).
 template <int D>
 __device__ inline void dvdk_block(KvState<D>& st, const TrReader<D>& tr, uint32_t Qt, uint32_t Ot, int t0,
                                   const bf16x8 (&pf)[2], const bf16x8 (&dsf)[2]) {
@@ -142,18 +146,20 @@ __device__ inline void dvdk_block(KvState<D>& st, const TrReader<D>& tr, uint32_
 
 // The wave's 32 keys against the 32-query block qb of the tile (rows
 // 32 qb .. 32 qb + 31): S, dP - Delta, P, dS, then dV^T += dO^T P and
-// dK^T += Q^T dS over query slots 2qb, 2qb + 1.
+// dK^T += Q^T dS over that block's two 16-query slots.  rq and tq carry the
+// block's row offset in their lane bases, so the tile offsets and the
+// per-step offsets fold into the LDS instructions' immediates.
 template <int D>
-__device__ inline void dkdv_block(KvState<D>& st, const RowReader<D>& rr, const TrReader<D>& tr, uint32_t Qt,
-                                  uint32_t Ot, uint32_t Vw, uint32_t Nl, uint32_t NDt, uint32_t QDt, int32_t qa0,
+__device__ inline void dkdv_block(KvState<D>& st, const RowReader<D>& rq, const TrReader<D>& tq, uint32_t Qt,
+                                  uint32_t Ot, uint32_t vb, uint32_t Nl, uint32_t NDt, uint32_t QDt, int32_t qa0,
                                   int qb, int32_t Lq, bool mask, bool docs, float c, int lane) {
   const int hh = lane >> 5;
   f32x16 s, dp;
   bf16x8 pf[2], dsf[2];
-  sdp_block<D>(st, rr, Qt, Ot, Vw, NDt, qb, s, dp, lane);
+  sdp_block<D>(st, rq, Qt, Ot, vb, NDt, qb, s, dp, lane);
   if (mask) dkdv_mask<D>(st, s, QDt, qa0, qb, Lq, docs, hh);
   pds_block(s, dp, Nl, qb, c, pf, dsf, hh);
-  dvdk_block<D>(st, tr, Qt, Ot, 2 * qb, pf, dsf);
+  dvdk_block<D>(st, tq, Qt, Ot, 0, pf, dsf);
 }
 
 __device__ inline void lds_st4(uint32_t a, const f32x4& x) {
@@ -307,8 +313,14 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
   const int32_t kd_hi = docs ? ks.doc[wlast] : 0;
   const float c = a.scale * LOG2E;
 
-  const RowReader<D> rr(lane);
-  const TrReader<D> tr(lane);
+  // lane bases with this wave's query half (rows 32 qh ..) and V rows folded
+  // in; the XOR-ed chunk and d-block steps act on bits the offsets leave clear
+  RowReader<D> rq(lane);
+  TrReader<D> tq(lane);
+  const uint32_t vb = Vw + rq.base;
+  rq.base += (uint32_t)(qh * 32 * 2 * D);
+  tq.b0 += (uint32_t)(qh * 32 * 2 * D);
+  tq.b1 += (uint32_t)(qh * 32 * 2 * D);
 
   wait_vm0();
   if (nitems > 0) prepare(S0 + L0, S0 + N0);
@@ -328,7 +340,7 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
     }
     live = __builtin_amdgcn_readfirstlane((int)live) != 0;   // wave-uniform: scalar branches
     full = __builtin_amdgcn_readfirstlane((int)full) != 0;
-    if (live) dkdv_block<D>(st, rr, tr, Qc, Oc, Vw, Lc, Dc, Xc, qa0, qh, Lq, !full, docs, c, lane);
+    if (live) dkdv_block<D>(st, rq, tq, Qc, Oc, vb, Lc, Dc, Xc, qa0, qh, Lq, !full, docs, c, lane);
     wait_vm0();
     if (it + 1 < nitems) prepare(Ln, Dn);
     __syncthreads();
