@@ -12,16 +12,16 @@
 //   dkdv (KV-outer): a work-group of 8 waves (two per SIMD) owns 128 keys of
 //     one KV head and streams 64-row tiles of Q and dO for every query head
 //     of the GQA group through LDS (direct-to-LDS loads, double-buffered).
-//     Wave w takes keys 32(w % 4) .. +31 (their K rows in VGPRs as MFMA B
-//     operands, their V rows resident in LDS, their dK^T and dV^T in
-//     accumulators) against query rows 32(w / 4) .. +31 of each tile.  Per
-//     tile: S = Q K^T, dP = dO V^T - Delta (A operands read row-wise; the dP
-//     accumulator starts at -Delta), P = exp2(S c + nl) with nl = -LSE log2 e,
-//     dS = P dP, then dV^T += dO^T P and dK^T += Q^T dS (A operands read with
-//     the LDS transpose read; P and dS go from the accumulator layout straight
-//     into the B operand).  4 MFMA products per (query, key) pair.  The two
-//     waves of a key block sum their partial dK, dV through LDS at the end;
-//     the softmax scale of dK is applied once, there.
+//     The work-group's K and V rows stay resident in LDS.  Wave w takes keys
+//     32(w % 4) .. +31 (their dK^T, dV^T accumulators in VGPRs) against query
+//     rows 32(w / 4) .. +31 of each tile.  Per tile: S = Q K^T,
+//     dP = dO V^T - Delta (row reads of both operands; the dP accumulator
+//     starts at -Delta), P = exp2(S c + nl) with nl = -LSE log2 e, dS = P dP,
+//     then dV^T += dO^T P and dK^T += Q^T dS (A operands read with the LDS
+//     transpose read; P and dS go from the accumulator layout straight into
+//     the B operand).  4 MFMA products per (query, key) pair.  The two waves
+//     of a key block sum their partial dK, dV through LDS at the end; the
+//     softmax scale of dK is applied once, there.
 //   dq (Q-outer): a work-group of 8 waves (two per SIMD) owns 64 query rows
 //     of 4 query heads sharing a KV head, 32 rows of one head per wave (like
 //     the forward), and streams 64-key tiles of K and V.  Per tile:
@@ -62,39 +62,17 @@ __device__ inline float neg_lse2(float lse) { return lse == -INFINITY ? -INFINIT
 
 // ============================== dK, dV ======================================
 
+// K rows sit this many bytes after the V rows in LDS (one 128-key tile)
+template <int D>
+constexpr uint32_t KV_GAP = 128 * D * 2;
+
 template <int D>
 struct KvState {
-  bf16x8 kf[D / 16];               // this wave's 32 keys as B operands (V is read from LDS)
   f32x16 dka[D / 32], dva[D / 32]; // dK^T (unscaled), dV^T accumulators [d block]
   int32_t qlim;                    // queries [qlim, ..) see this lane's key causally
   int32_t kdoc;
   bool kvalid;
 };
-
-// S and dP - Delta of the 32-query block qb of the tile.  Accumulator element
-// r: key = the lane's key, query row qb*32 + 8(r/4) + 4hh + r%4.  rq reads
-// rows of block qb (its base holds the block offset); vb is the lane's
-// address in the wave's V rows.
-template <int D>
-__device__ inline void sdp_block(const KvState<D>& st, const RowReader<D>& rq, uint32_t Qt, uint32_t Ot,
-                                 uint32_t vb, uint32_t NDt, int qb, f32x16& s, f32x16& dp, int lane) {
-  const int hh = lane >> 5;
-  f32x16 init;   // -Delta of the element's query row
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f32x4 d4 = lds_f4(NDt + 4 * (qb * 32 + j * 8 + hh * 4));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) init[j * 4 + i] = d4[i];
-  }
-  s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq.at(Qt, 0, 0), st.kf[0], f32x16{}, 0, 0, 0);
-  dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq.at(Ot, 0, 0), lds_ld16(vb), init, 0, 0, 0);
-#pragma unroll
-  for (int kd = 1; kd < D / 16; ++kd) {
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq.at(Qt, 0, kd), st.kf[kd], s, 0, 0, 0);
-    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq.at(Ot, 0, kd), lds_ld16(vb ^ (uint32_t)(kd << 5)), dp, 0,
-                                                 0, 0);
-  }
-}
 
 // Element mask of block qb: S = -inf where the lane's key is not visible.
 template <int D>
@@ -112,54 +90,101 @@ __device__ inline void dkdv_mask(const KvState<D>& st, f32x16& s, uint32_t QDt, 
   }
 }
 
-// P and dS of block qb as B operands (query slots t = 2qb, 2qb + 1).
-__device__ inline void pds_block(const f32x16& s, const f32x16& dp, uint32_t Nl, int qb, float c,
-                                 bf16x8 (&pf)[2], bf16x8 (&dsf)[2], int hh) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f32x4 n4 = lds_f4(Nl + 4 * (qb * 32 + j * 8 + hh * 4));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = j * 4 + i;
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, n4[i]));
-      pf[r >> 3][r & 7] = (__bf16)p;
-      dsf[r >> 3][r & 7] = (__bf16)(p * dp[r]);
-    }
-  }
-}
-
-// dV^T += dO^T P, dK^T += Q^T dS over the query slots t0, t0 + 1 (slots
-// counted from the row offset held in tr's bases).
-template <int D>
-__device__ inline void dvdk_block(KvState<D>& st, const TrReader<D>& tr, uint32_t Qt, uint32_t Ot, int t0,
-                                  const bf16x8 (&pf)[2], const bf16x8 (&dsf)[2]) {
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int t = t0 + u;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      st.dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr.at(Ot, 16 * t, db), pf[u], st.dva[db], 0, 0, 0);
-      st.dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr.at(Qt, 16 * t, db), dsf[u], st.dka[db], 0, 0, 0);
-    }
-  }
-}
-
 // The wave's 32 keys against the 32-query block qb of the tile (rows
-// 32 qb .. 32 qb + 31): S, dP - Delta, P, dS, then dV^T += dO^T P and
+// 32 qb .. 32 qb + 31): S and dP - Delta (accumulator element r: key = the
+// lane's key, query row qb*32 + 8(r/4) + 4hh + r%4; the dP accumulator starts
+// at -Delta), P = exp2(S c + nl), dS = P dP, then dV^T += dO^T P and
 // dK^T += Q^T dS over that block's two 16-query slots.  rq and tq carry the
-// block's row offset in their lane bases, so the tile offsets and the
+// block's row offset in their lane bases; vb is the lane's address in the
+// wave's V rows (its K rows KV_GAP bytes on), so the tile offsets and the
 // per-step offsets fold into the LDS instructions' immediates.
+//
+// Explicit software pipeline (scheduling walls keep the order): operand
+// reads run two MFMAs ahead through a two-entry register ring, and slot 1's
+// P/dS VALU work is spread over slot 0's gradient MFMAs.
 template <int D>
 __device__ inline void dkdv_block(KvState<D>& st, const RowReader<D>& rq, const TrReader<D>& tq, uint32_t Qt,
                                   uint32_t Ot, uint32_t vb, uint32_t Nl, uint32_t NDt, uint32_t QDt, int32_t qa0,
                                   int qb, int32_t Lq, bool mask, bool docs, float c, int lane) {
+  constexpr int NKD = D / 16, NDB = D / 32;
   const int hh = lane >> 5;
   f32x16 s, dp;
-  bf16x8 pf[2], dsf[2];
-  sdp_block<D>(st, rq, Qt, Ot, vb, NDt, qb, s, dp, lane);
+  {
+    f32x16 init;   // -Delta of the element's query row
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 d4 = lds_f4(NDt + 4 * (qb * 32 + j * 8 + hh * 4));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) init[j * 4 + i] = d4[i];
+    }
+    bf16x8 ra[2], ro[2], rv[2], rk[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      ra[k] = rq.at(Qt, 0, k);
+      ro[k] = rq.at(Ot, 0, k);
+      rv[k] = lds_ld16(vb ^ (uint32_t)(k << 5));
+      rk[k] = lds_ld16((vb ^ (uint32_t)(k << 5)) + KV_GAP<D>);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[kd & 1], rk[kd & 1], kd ? s : f32x16{}, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ro[kd & 1], rv[kd & 1], kd ? dp : init, 0, 0, 0);
+      if (kd + 2 < NKD) {
+        ra[kd & 1] = rq.at(Qt, 0, kd + 2);
+        ro[kd & 1] = rq.at(Ot, 0, kd + 2);
+        rv[kd & 1] = lds_ld16(vb ^ (uint32_t)((kd + 2) << 5));
+        rk[kd & 1] = lds_ld16((vb ^ (uint32_t)((kd + 2) << 5)) + KV_GAP<D>);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
   if (mask) dkdv_mask<D>(st, s, QDt, qa0, qb, Lq, docs, hh);
-  pds_block(s, dp, Nl, qb, c, pf, dsf, hh);
-  dvdk_block<D>(st, tq, Qt, Ot, 0, pf, dsf);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // gradient operands of MFMA pair m (slot m / NDB, d block m % NDB)
+  bf16x8 go[2], gq[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    go[m] = tq.at(Ot, 16 * (m / NDB), m % NDB);
+    gq[m] = tq.at(Qt, 16 * (m / NDB), m % NDB);
+  }
+  bf16x8 pf[2], dsf[2];
+  auto pds = [&](int r, const f32x4& n4) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, n4[r & 3]));
+    pf[r >> 3][r & 7] = (__bf16)p;
+    dsf[r >> 3][r & 7] = (__bf16)(p * dp[r]);
+  };
+  {
+    const f32x4 n0 = lds_f4(Nl + 4 * (qb * 32 + 0 * 8 + hh * 4));
+    const f32x4 n1 = lds_f4(Nl + 4 * (qb * 32 + 1 * 8 + hh * 4));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pds(r, n0);
+#pragma unroll
+    for (int r = 4; r < 8; ++r) pds(r, n1);
+  }
+  const f32x4 n2 = lds_f4(Nl + 4 * (qb * 32 + 2 * 8 + hh * 4));
+  const f32x4 n3 = lds_f4(Nl + 4 * (qb * 32 + 3 * 8 + hh * 4));
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int PER = 8 / NDB;   // slot-1 elements per slot-0 MFMA pair
+#pragma unroll
+  for (int m = 0; m < 2 * NDB; ++m) {
+    const int u = m / NDB, db = m % NDB;
+    st.dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(go[m & 1], pf[u], st.dva[db], 0, 0, 0);
+    st.dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gq[m & 1], dsf[u], st.dka[db], 0, 0, 0);
+    if (m + 2 < 2 * NDB) {
+      go[m & 1] = tq.at(Ot, 16 * ((m + 2) / NDB), (m + 2) % NDB);
+      gq[m & 1] = tq.at(Qt, 16 * ((m + 2) / NDB), (m + 2) % NDB);
+    }
+    if (m < NDB) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int r = 8 + m * PER + e;
+        pds(r, r < 12 ? n2 : n3);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 __device__ inline void lds_st4(uint32_t a, const f32x4& x) {
@@ -216,10 +241,11 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
   constexpr uint32_t TB = BQ * D * 2, RW = BQ * 4;
   constexpr uint32_t Q0 = 0, Q1 = TB, O0 = 2 * TB, O1 = 3 * TB;
   constexpr uint32_t L0 = 4 * TB, L1 = L0 + RW, N0 = L1 + RW, N1 = N0 + RW, X0 = N1 + RW, X1 = X0 + RW;
-  constexpr uint32_t VT = X1 + RW;
+  constexpr uint32_t VT = X1 + RW;   // V rows, then K rows KV_GAP bytes on
   static_assert(4 * BKW * D * 4 <= 4 * TB, "parked accumulators must fit in the tile area");
   static_assert(VT % 16 == 0, "V tile alignment");
-  __shared__ __attribute__((aligned(16))) char smem[VT + BKG * D * 2];
+  static_assert(KV_GAP<D> == BKG * D * 2, "K rows follow the V rows");
+  __shared__ __attribute__((aligned(16))) char smem[VT + 2 * BKG * D * 2];
   const uint32_t S0 = lds_addr(smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -285,8 +311,10 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
     if (k0 + BKG <= Lk) {
       const TileLoader<D, BKG, KNW> ldv(a.kv_stride * 2, wave, lane);
       ldv.load(S0 + VT, (const char*)(a.v + (int64_t)k0 * a.kv_stride + (int64_t)kvh * D));
+      ldv.load(S0 + VT + KV_GAP<D>, (const char*)(a.k + (int64_t)k0 * a.kv_stride + (int64_t)kvh * D));
     } else {
       tile_load_lds<D, BKG, KNW>(S0 + VT, a.v + (int64_t)kvh * D, a.kv_stride, k0, Lk, wave, lane);
+      tile_load_lds<D, BKG, KNW>(S0 + VT + KV_GAP<D>, a.k + (int64_t)kvh * D, a.kv_stride, k0, Lk, wave, lane);
     }
     issue(0, S0 + Q0, S0 + O0, S0 + L0, S0 + N0, S0 + X0);
   }
@@ -295,9 +323,6 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
   KvState<D> st;
   {
     const int32_t mykey = min(wk0 + lq, Lk - 1);
-    const bf16x8* ksrc = (const bf16x8*)(a.k + (int64_t)mykey * a.kv_stride + (int64_t)kvh * D + hh * 8);
-#pragma unroll
-    for (int kd = 0; kd < D / 16; ++kd) st.kf[kd] = ksrc[kd * 2];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) { st.dka[db] = f32x16{}; st.dva[db] = f32x16{}; }
     st.qlim = causal ? span_count_lt(qs, span_pos(ks, mykey)) : 0;
