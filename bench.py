@@ -313,6 +313,43 @@ def cpu_baseline(wl):
             "seconds": t, "torch_threads": torch.get_num_threads()}
 
 
+XGMI_LINK_GBS = 153.0   # one xGMI link, per direction (the ring's neighbour link)
+
+
+def ring_overlap(wl, cp, torch, steps, ms_plain):
+    """One ring rank's step with the ring's traffic emulated on a second
+    stream (cp_ring_emulate_overlap): each ring step's KV shard arrives through
+    a strided copy issued one step ahead, and in the backward each step's
+    dK/dV shard leaves through a copy.  Reports the step time beside the plain
+    one, the bytes one ring step moves, and what those bytes take over one
+    xGMI link against the compute of one ring step."""
+    ws = cp.workspace(cp.cp_ring_overlap_workspace_bytes(wl.sh, wl.S, wl.P, cp.CP_BF16, True))
+    side = torch.cuda.Stream()
+
+    def run():
+        cp.cp_ring_emulate_overlap(wl.sh, wl.S, wl.P, 0, wl.q, wl.k, wl.v, None, wl.o, wl.lse, wl.dout,
+                                   wl.dq, wl.dk, wl.dv, workspace=ws, copy_stream=side)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    n, kvrow = wl.S // wl.P, wl.hkv * wl.d
+    kv_b = 2 * n * kvrow * 2          # K and V shard, bf16
+    grad_b = 2 * n * kvrow * 4        # dK and dV shard, fp32
+    ring_steps = 2 * (wl.P - 1)       # forward and backward steps that receive a shard
+    return {"ms_per_step_plain": round(ms_plain, 4), "ms_per_step_with_traffic": round(ms, 4),
+            "overhead_frac": round(ms / ms_plain - 1.0, 4),
+            "bytes_per_ring_step_fwd": kv_b, "bytes_per_ring_step_bwd": kv_b + grad_b,
+            "copies_per_step": ring_steps, "grad_sends_per_step": wl.P,
+            "compute_ms_per_ring_step": round(ms_plain / (2 * wl.P), 4),
+            "xgmi_link_ms_per_ring_step_bwd": round((kv_b + grad_b) / (XGMI_LINK_GBS * 1e9) * 1e3, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -406,6 +443,8 @@ def main():
             bal[f"P{P}"] = {"zigzag_max_over_mean": round(float(zz.max() / zz.mean()), 3),
                             "doc_aware_max_over_mean": round(float(rw.max() / rw.mean()), 3)}
         out["ring_balance"] = bal
+    if wl.name in ("ring_128k", "usp_1m"):
+        out["ring_overlap"] = ring_overlap(wl, cp, torch, max(1, min(args.steps, 3)), ms)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

@@ -198,6 +198,31 @@ cp_status cp_ring_emulate(const cp_shape *sh, int64_t S, int32_t P, int32_t rank
                           float *step_o, float *step_lse,
                           void *workspace, size_t ws_bytes, void *stream);
 
+/* Workspace bytes cp_ring_emulate_overlap needs (0 on bad args). */
+size_t cp_ring_overlap_workspace_bytes(const cp_shape *sh, int64_t S, int32_t P,
+                                       cp_dtype o_dtype, int32_t backward);
+
+/* cp_ring_emulate for one rank (rank >= 0, no per-step capture) with the
+ * ring's traffic emulated on a second stream, so that its cost beside the
+ * compute can be measured ([MaxText] diagram text, P2P: each GPU computes with
+ * the chunk it holds while the next one arrives; section "헤드를 나누거나,
+ * KV를 돌리거나": the ring can overlap communication with computation).  Step
+ * s >= 1 of the forward and of the backward reads its KV shard from a
+ * double-buffered receive area in the workspace, filled on copy_stream one
+ * step ahead (a strided copy of the shard's rows, i.e. what the neighbour
+ * sends); after each backward step the shard's dK, dV rows are copied into a
+ * send area on copy_stream (what goes back to the owner).  Events order the
+ * copies against the compute; when the work queued on `stream` completes, so
+ * has the copy work.  Outputs are bitwise those of cp_ring_emulate for the
+ * same rank.  copy_stream must differ from stream (both at the default
+ * priority).  Workspace: >= cp_ring_overlap_workspace_bytes, 256-byte
+ * aligned, caller-owned; calls that share a workspace must not overlap. */
+cp_status cp_ring_emulate_overlap(const cp_shape *sh, int64_t S, int32_t P, int32_t rank,
+                                  const void *q, const void *k, const void *v, const int32_t *doc,
+                                  void *o, cp_dtype o_dtype, float *lse,
+                                  const void *dout, float *dq, float *dk, float *dv,
+                                  void *workspace, size_t ws_bytes, void *stream, void *copy_stream);
+
 /* Workspace bytes cp_ulysses_share needs (0 on bad args). */
 size_t cp_ulysses_workspace_bytes(const cp_shape *sh_full, int64_t S, int32_t sp, int32_t backward);
 

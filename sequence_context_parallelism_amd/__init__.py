@@ -24,6 +24,7 @@ EXPORTED = (
     "cp_attn_chunk_fwd", "cp_lse_merge", "cp_attn_delta", "cp_attn_chunk_bwd",
     "cp_attn_chunk_bwd_dkdv", "cp_attn_chunk_bwd_dq",
     "cp_zigzag_layout", "cp_ring_schedule", "cp_ring_workspace_bytes", "cp_ring_emulate",
+    "cp_ring_overlap_workspace_bytes", "cp_ring_emulate_overlap",
     "cp_ulysses_workspace_bytes", "cp_ulysses_share", "cp_allgather_workspace_bytes", "cp_allgather_share",
     "cp_chunk_work", "cp_balanced_pairs",
     "cp_a2a_tokens_to_heads", "cp_a2a_heads_to_tokens",
@@ -73,6 +74,9 @@ def load(path: str = LIB_PATH):
         "cp_ring_schedule": (I32, [I64, I32, I32, I32, ctypes.POINTER(ctypes.c_int32),
                                    ctypes.POINTER(ctypes.c_int8)]),
         "cp_ring_workspace_bytes": (SZ, [SH, I64, I32, I32, I32, I32]),
+        "cp_ring_overlap_workspace_bytes": (SZ, [SH, I64, I32, I32, I32]),
+        "cp_ring_emulate_overlap": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P,
+                                          P, SZ, P, P]),
         "cp_ring_emulate": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, P, P,
                                   P, SZ, P]),
         "cp_ulysses_workspace_bytes": (SZ, [SH, I64, I32, I32]),
@@ -107,7 +111,7 @@ def _ptr(t):
 
 def _stream(stream):
     if stream is not None:
-        return ctypes.c_void_p(stream)
+        return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))   # torch stream or raw handle
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -212,6 +216,20 @@ def cp_ring_emulate(shape, S, P, rank, q, k, v, doc, o, lse, dout=None, dq=None,
                                _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                                _ptr(dv), _ptr(step_o), _ptr(step_lse), _ptr(workspace), ws_bytes,
                                _stream(stream)))
+
+
+def cp_ring_overlap_workspace_bytes(shape, S, P, o_dtype, backward):
+    return load().cp_ring_overlap_workspace_bytes(ctypes.byref(shape), S, P, o_dtype, int(bool(backward)))
+
+
+def cp_ring_emulate_overlap(shape, S, P, rank, q, k, v, doc, o, lse, dout=None, dq=None, dk=None, dv=None,
+                            workspace=None, stream=None, copy_stream=None):
+    lib = load()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.cp_ring_emulate_overlap(ctypes.byref(shape), S, P, rank, _ptr(q), _ptr(k), _ptr(v), _ptr(doc),
+                                       _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                       _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream),
+                                       _stream(copy_stream)))
 
 
 def cp_ulysses_workspace_bytes(shape, S, sp, backward):

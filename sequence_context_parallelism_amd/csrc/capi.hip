@@ -174,6 +174,75 @@ cp_status check_ring_args(const cp_shape* sh, int64_t S, int32_t P, int32_t rank
   return CP_OK;
 }
 
+// Emulated ring traffic (one rank): the KV shard each step reads arrives in a
+// double-buffered receive area through a copy on a second stream, issued one
+// step ahead; in the backward, each step's finished dK/dV shard leaves through
+// a copy into a send area.  Events order the copies against the compute.
+struct RingOverlap {
+  hipStream_t cs;
+  char* recv[2];         // compact K rows then V rows of one shard, [n, hkv, d]
+  float* send;           // dK rows then dV rows of one shard, fp32 [n, hkv, d]
+};
+
+struct OverlapLayout {
+  size_t recv0, recv1, send, total;
+};
+
+OverlapLayout overlap_layout(const cp_shape* sh, int64_t n, bool backward, size_t base) {
+  OverlapLayout L{};
+  const size_t kv = align256((size_t)2 * n * sh->hkv * sh->d * elt_size(sh->dtype));
+  L.recv0 = base;
+  L.recv1 = L.recv0 + kv;
+  L.send = L.recv1 + kv;
+  L.total = L.send + (backward ? align256((size_t)2 * n * sh->hkv * sh->d * 4) : 0);
+  return L;
+}
+
+// Events of one call (timing off), released when the call returns; a pending
+// event is freed by the runtime once it completes.
+struct EventSet {
+  std::vector<hipEvent_t> e;
+  ~EventSet() {
+    for (hipEvent_t x : e) (void)hipEventDestroy(x);
+  }
+  hipError_t make(size_t count) {
+    e.assign(count, nullptr);
+    for (size_t i = 0; i < count; ++i) {
+      hipError_t r = hipEventCreateWithFlags(&e[i], hipEventDisableTiming);
+      if (r != hipSuccess) return r;
+    }
+    return hipSuccess;
+  }
+};
+
+// Argument checks shared by the ring entry points.
+cp_status ring_args(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, const void* q, const void* k,
+                    const void* v, void* o, cp_dtype o_dtype, float* lse, const void* dout, float* dq, float* dk,
+                    float* dv) {
+  CP_TRY(check_ring_args(sh, S, P, rank));
+  if (!valid_dtype(o_dtype)) return fail(CP_ERR_ARG, "unknown o_dtype");
+  CP_TRY(check_ptr(q, "q"));
+  CP_TRY(check_ptr(k, "k"));
+  CP_TRY(check_ptr(v, "v"));
+  CP_TRY(check_ptr(o, "o"));
+  if (!lse) return fail(CP_ERR_ARG, "lse is NULL");
+  if (dout != nullptr) {
+    CP_TRY(check_ptr(dout, "dout"));
+    CP_TRY(check_ptr(dq, "dq"));
+    CP_TRY(check_ptr(dk, "dk"));
+    CP_TRY(check_ptr(dv, "dv"));
+  }
+  return CP_OK;
+}
+
+cp_status check_workspace(const void* workspace, size_t ws_bytes, size_t need) {
+  if (need == 0) return CP_OK;
+  if (!workspace) return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+  if (ws_bytes < need) return fail(CP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(CP_ERR_ALIGN, "workspace must be 256-byte aligned");
+  return CP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -304,38 +373,20 @@ size_t cp_ring_workspace_bytes(const cp_shape* sh, int64_t S, int32_t P, int32_t
   return ring_layout(sh, S / P, o_dtype, backward != 0).total;
 }
 
-cp_status cp_ring_emulate(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, const void* q, const void* k,
-                          const void* v, const int32_t* doc, void* o, cp_dtype o_dtype, float* lse,
-                          const void* dout, float* dq, float* dk, float* dv, float* step_o, float* step_lse,
-                          void* workspace, size_t ws_bytes, void* stream) {
-  CP_TRY(check_ring_args(sh, S, P, rank));
-  if (!valid_dtype(o_dtype)) return fail(CP_ERR_ARG, "unknown o_dtype");
-  CP_TRY(check_ptr(q, "q"));
-  CP_TRY(check_ptr(k, "k"));
-  CP_TRY(check_ptr(v, "v"));
-  CP_TRY(check_ptr(o, "o"));
-  if (!lse) return fail(CP_ERR_ARG, "lse is NULL");
+}  // extern "C"
+
+namespace {
+
+// The ring driver; with `ov` (a single rank, no per-step capture) the steps
+// read their KV shard from the receive area (see RingOverlap).
+cp_status ring_drive(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, const void* q, const void* k,
+                     const void* v, const int32_t* doc, void* o, cp_dtype o_dtype, float* lse, const void* dout,
+                     float* dq, float* dk, float* dv, float* step_o, float* step_lse, char* ws, hipStream_t st,
+                     const RingOverlap* ov) {
   const bool backward = dout != nullptr;
-  if (backward) {
-    CP_TRY(check_ptr(dout, "dout"));
-    CP_TRY(check_ptr(dq, "dq"));
-    CP_TRY(check_ptr(dk, "dk"));
-    CP_TRY(check_ptr(dv, "dv"));
-  }
-  if ((step_o == nullptr) != (step_lse == nullptr))
-    return fail(CP_ERR_ARG, "step_o and step_lse must both be given or both be NULL");
-  if (step_o && rank < 0) return fail(CP_ERR_ARG, "per-step capture needs a single rank");
-  if (step_o) CP_TRY(check_ptr(step_o, "step_o"));
   const int64_t n = S / P;                       // rows per rank = 2c
   const int32_t c = (int32_t)(S / (2 * P));
   const RingLayout lay = ring_layout(sh, n, o_dtype, backward);
-  if (lay.total > 0) {
-    if (!workspace) return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes required", lay.total);
-    if (ws_bytes < lay.total) return fail(CP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, lay.total);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(CP_ERR_ALIGN, "workspace must be 256-byte aligned");
-  }
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
   float* acc_o_ws = (float*)(ws + lay.acc_o);
   float* part_o = (float*)(ws + lay.part_o);
   float* part_lse = (float*)(ws + lay.part_lse);
@@ -352,6 +403,51 @@ cp_status cp_ring_emulate(const cp_shape* sh, int64_t S, int32_t P, int32_t rank
     CP_TRY_HIP(launch_fill_zero(S * kvrow, dv, st), "zero dv");
   }
 
+  // emulated traffic: events [0] start, [1] forward end, [2] end; then per
+  // pass (forward, backward) P "shard received" and P "step computed" events
+  EventSet ev;
+  cp_shape shc = *sh;                                     // receive rows are compact
+  shc.kv_stride = kvrow;
+  const size_t shard_b = (size_t)n * kvrow * in_esz;     // K (or V) rows of one shard
+  if (ov) {
+    CP_TRY_HIP(ev.make(3 + 4 * (size_t)P), "ring events");
+    CP_TRY_HIP(hipEventRecord(ev.e[0], st), "ring event");
+    CP_TRY_HIP(hipStreamWaitEvent(ov->cs, ev.e[0], 0), "ring wait");   // earlier readers of the areas
+  }
+  auto ev_ready = [&](int pass, int32_t s) { return ev.e[3 + (size_t)pass * 2 * P + s]; };
+  auto ev_done = [&](int pass, int32_t s) { return ev.e[3 + (size_t)pass * 2 * P + P + s]; };
+  // Before step s computes: the shard of step s + 1 into recv[(s + 1) & 1],
+  // once step s - 1 (its last reader) is done.
+  auto prefetch = [&](int pass, int32_t r, int32_t s) -> hipError_t {
+    if (!ov || s + 1 >= P) return hipSuccess;
+    hipError_t e = hipSuccess;
+    if (s >= 2) e = hipStreamWaitEvent(ov->cs, ev_done(pass, s - 1), 0);
+    const int32_t j = ((r - (s + 1)) % P + P) % P;
+    char* dst = ov->recv[(s + 1) & 1];
+    const size_t pitch = (size_t)sh->kv_stride * in_esz, width = (size_t)kvrow * in_esz;
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(dst, width, (const char*)k + (size_t)j * n * pitch, pitch, width, n,
+                           hipMemcpyDeviceToDevice, ov->cs);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(dst + shard_b, width, (const char*)v + (size_t)j * n * pitch, pitch, width, n,
+                           hipMemcpyDeviceToDevice, ov->cs);
+    if (e == hipSuccess) e = hipEventRecord(ev_ready(pass, s + 1), ov->cs);
+    return e;
+  };
+  // The KV operands of step s: in place for s = 0 (the rank's own shard) or
+  // without emulation, else the receive area once its copy has landed.
+  auto step_kv = [&](int pass, int32_t s, int32_t j, const char*& kj, const char*& vj,
+                     const cp_shape*& shs) -> hipError_t {
+    shs = sh;
+    kj = (const char*)k + (size_t)j * n * sh->kv_stride * in_esz;
+    vj = (const char*)v + (size_t)j * n * sh->kv_stride * in_esz;
+    if (!ov || s == 0) return hipSuccess;
+    shs = &shc;
+    kj = ov->recv[s & 1];
+    vj = ov->recv[s & 1] + shard_b;
+    return hipStreamWaitEvent(st, ev_ready(pass, s), 0);
+  };
+
   const int32_t r0 = rank < 0 ? 0 : rank, r1 = rank < 0 ? P : rank + 1;
   for (int32_t r = r0; r < r1; ++r) {
     const int64_t out_row0 = rank < 0 ? (int64_t)r * n : 0;       // row offset into o / dq
@@ -363,18 +459,22 @@ cp_status cp_ring_emulate(const cp_shape* sh, int64_t S, int32_t P, int32_t rank
 
     for (int32_t s = 0; s < P; ++s) {
       const int32_t j = ((r - s) % P + P) % P;
-      const char* kj = (const char*)k + (size_t)j * n * sh->kv_stride * in_esz;
-      const char* vj = (const char*)v + (size_t)j * n * sh->kv_stride * in_esz;
+      const char *kj, *vj;
+      const cp_shape* shs;
+      CP_TRY_HIP(prefetch(0, r, s), "ring receive copy");
+      CP_TRY_HIP(step_kv(0, s, j, kj, vj, shs), "ring wait");
       const cp_span ks = run_span((int64_t)j * c, c, (int64_t)(2 * P - 1 - j) * c, c, doc ? doc + j * n : nullptr);
       // bf16 steps after the first merge into the running result in the
       // forward kernel's epilogue (no partial round trip through HBM)
       if (s > 0 && !step_o && sh->dtype == CP_BF16) {
-        CP_TRY_HIP(run_fwd(sh, qr, qs, kj, vj, ks, acc_o, CP_F32, lse_r, n, st, true), "ring forward step");
+        CP_TRY_HIP(run_fwd(shs, qr, qs, kj, vj, ks, acc_o, CP_F32, lse_r, n, st, true), "ring forward step");
+        if (ov) CP_TRY_HIP(hipEventRecord(ev_done(0, s), st), "ring event");
         continue;
       }
       float* so = step_o ? step_o + (size_t)s * n * orow : (s == 0 ? acc_o : part_o);
       float* sl = step_lse ? step_lse + (size_t)s * sh->hq * n : (s == 0 ? lse_r : part_lse);
-      CP_TRY_HIP(run_fwd(sh, qr, qs, kj, vj, ks, so, CP_F32, sl, n, st), "ring forward step");
+      CP_TRY_HIP(run_fwd(shs, qr, qs, kj, vj, ks, so, CP_F32, sl, n, st), "ring forward step");
+      if (ov) CP_TRY_HIP(hipEventRecord(ev_done(0, s), st), "ring event");
       if (s == 0) {
         if (step_o) {
           CP_TRY_HIP(launch_copy_f32(n * orow, so, acc_o, st), "ring copy");
@@ -385,6 +485,10 @@ cp_status cp_ring_emulate(const cp_shape* sh, int64_t S, int32_t P, int32_t rank
       }
     }
     if (o_dtype == CP_BF16) CP_TRY_HIP(launch_f32_to_bf16(n * orow, acc_o, (__bf16*)o_r, st), "ring convert");
+    if (ov) {   // the backward pass refills the receive areas after the forward's last reads
+      CP_TRY_HIP(hipEventRecord(ev.e[1], st), "ring event");
+      CP_TRY_HIP(hipStreamWaitEvent(ov->cs, ev.e[1], 0), "ring wait");
+    }
 
     if (backward) {
       const char* dout_r = (const char*)dout + (size_t)out_row0 * orow * in_esz;
@@ -393,15 +497,72 @@ cp_status cp_ring_emulate(const cp_shape* sh, int64_t S, int32_t P, int32_t rank
                  "ring delta");
       for (int32_t s = 0; s < P; ++s) {
         const int32_t j = ((r - s) % P + P) % P;
-        const char* kj = (const char*)k + (size_t)j * n * sh->kv_stride * in_esz;
-        const char* vj = (const char*)v + (size_t)j * n * sh->kv_stride * in_esz;
+        const char *kj, *vj;
+        const cp_shape* shs;
+        CP_TRY_HIP(prefetch(1, r, s), "ring receive copy");
+        CP_TRY_HIP(step_kv(1, s, j, kj, vj, shs), "ring wait");
         const cp_span ks = run_span((int64_t)j * c, c, (int64_t)(2 * P - 1 - j) * c, c, doc ? doc + j * n : nullptr);
-        CP_TRY_HIP(run_bwd(sh, qr, qs, kj, vj, ks, dout_r, lse_r, dlt, n, dq_r, dk + (size_t)j * n * kvrow,
-                           dv + (size_t)j * n * kvrow, st), "ring backward step");
+        float* dkj = dk + (size_t)j * n * kvrow;
+        float* dvj = dv + (size_t)j * n * kvrow;
+        CP_TRY_HIP(run_bwd(shs, qr, qs, kj, vj, ks, dout_r, lse_r, dlt, n, dq_r, dkj, dvj, st), "ring backward step");
+        if (ov) {   // the step's dK/dV shard leaves for its owner
+          const size_t gb = (size_t)n * kvrow * 4;
+          CP_TRY_HIP(hipEventRecord(ev_done(1, s), st), "ring event");
+          CP_TRY_HIP(hipStreamWaitEvent(ov->cs, ev_done(1, s), 0), "ring wait");
+          CP_TRY_HIP(hipMemcpyAsync(ov->send, dkj, gb, hipMemcpyDeviceToDevice, ov->cs), "ring send copy");
+          CP_TRY_HIP(hipMemcpyAsync((char*)ov->send + gb, dvj, gb, hipMemcpyDeviceToDevice, ov->cs), "ring send copy");
+        }
       }
     }
   }
+  if (ov) {   // the call's completion on `stream` covers the copies too
+    CP_TRY_HIP(hipEventRecord(ev.e[2], ov->cs), "ring event");
+    CP_TRY_HIP(hipStreamWaitEvent(st, ev.e[2], 0), "ring wait");
+  }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status cp_ring_emulate(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, const void* q, const void* k,
+                          const void* v, const int32_t* doc, void* o, cp_dtype o_dtype, float* lse,
+                          const void* dout, float* dq, float* dk, float* dv, float* step_o, float* step_lse,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  CP_TRY(ring_args(sh, S, P, rank, q, k, v, o, o_dtype, lse, dout, dq, dk, dv));
+  if ((step_o == nullptr) != (step_lse == nullptr))
+    return fail(CP_ERR_ARG, "step_o and step_lse must both be given or both be NULL");
+  if (step_o && rank < 0) return fail(CP_ERR_ARG, "per-step capture needs a single rank");
+  if (step_o) CP_TRY(check_ptr(step_o, "step_o"));
+  CP_TRY(check_workspace(workspace, ws_bytes, ring_layout(sh, S / P, o_dtype, dout != nullptr).total));
+  return ring_drive(sh, S, P, rank, q, k, v, doc, o, o_dtype, lse, dout, dq, dk, dv, step_o, step_lse,
+                    (char*)workspace, (hipStream_t)stream, nullptr);
+}
+
+size_t cp_ring_overlap_workspace_bytes(const cp_shape* sh, int64_t S, int32_t P, cp_dtype o_dtype, int32_t backward) {
+  if (check_ring_args(sh, S, P, 0) != CP_OK || !valid_dtype(o_dtype)) return 0;
+  const int64_t n = S / P;
+  const size_t base = align256(ring_layout(sh, n, o_dtype, backward != 0).total);
+  return overlap_layout(sh, n, backward != 0, base).total;
+}
+
+cp_status cp_ring_emulate_overlap(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, const void* q,
+                                  const void* k, const void* v, const int32_t* doc, void* o, cp_dtype o_dtype,
+                                  float* lse, const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                                  size_t ws_bytes, void* stream, void* copy_stream) {
+  CP_TRY(ring_args(sh, S, P, rank, q, k, v, o, o_dtype, lse, dout, dq, dk, dv));
+  if (rank < 0) return fail(CP_ERR_ARG, "the traffic emulation runs one rank (rank >= 0)");
+  if (copy_stream == stream) return fail(CP_ERR_ARG, "copy_stream must differ from stream");
+  const bool backward = dout != nullptr;
+  const int64_t n = S / P;
+  const size_t base = align256(ring_layout(sh, n, o_dtype, backward).total);
+  const OverlapLayout L = overlap_layout(sh, n, backward, base);
+  CP_TRY(check_workspace(workspace, ws_bytes, L.total));
+  char* ws = (char*)workspace;
+  RingOverlap ov{(hipStream_t)copy_stream, {ws + L.recv0, ws + L.recv1}, (float*)(ws + L.send)};
+  return ring_drive(sh, S, P, rank, q, k, v, doc, o, o_dtype, lse, dout, dq, dk, dv, nullptr, nullptr, ws,
+                    (hipStream_t)stream, &ov);
 }
 
 size_t cp_ulysses_workspace_bytes(const cp_shape* sh, int64_t S, int32_t sp, int32_t backward) {

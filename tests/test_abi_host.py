@@ -116,6 +116,22 @@ def test_ring_and_ulysses_argument_errors(lib):
                               None, None, None, None, None, 0, None)
     assert st == cp.CP_ERR_ARG                                  # sp=4 does not divide hkv=2
     assert cp.cp_ulysses_workspace_bytes(sh, 1024, 2, True) == 4 * 1024 * 4
+    # the traffic emulation: one rank only, a distinct copy stream, its own workspace
+    S1 = ctypes.c_void_p(0x20000)
+    st = lib.cp_ring_emulate_overlap(ctypes.byref(sh), 1024, 8, -1, P, P, P, None, P, cp.CP_BF16, P,
+                                     None, None, None, None, None, 0, None, S1)
+    assert st == cp.CP_ERR_ARG                                  # rank -1
+    st = lib.cp_ring_emulate_overlap(ctypes.byref(sh), 1024, 8, 0, P, P, P, None, P, cp.CP_BF16, P,
+                                     None, None, None, None, None, 0, S1, S1)
+    assert st == cp.CP_ERR_ARG                                  # same stream twice
+    st = lib.cp_ring_emulate_overlap(ctypes.byref(sh), 1024, 8, 0, P, P, P, None, P, cp.CP_BF16, P,
+                                     None, None, None, None, None, 0, None, S1)
+    assert st == cp.CP_ERR_WORKSPACE
+    plain = cp.cp_ring_workspace_bytes(sh, 1024, 8, 0, cp.CP_BF16, True)
+    over = cp.cp_ring_overlap_workspace_bytes(sh, 1024, 8, cp.CP_BF16, True)
+    n, kvrow = 1024 // 8, sh.hkv * sh.d
+    assert over % 256 == 0 and over >= plain + 2 * (2 * n * kvrow * 2) + 2 * n * kvrow * 4
+    assert cp.cp_ring_overlap_workspace_bytes(sh, 1000, 8, cp.CP_BF16, True) == 0
 
 
 def _docs(S, seed, median):
