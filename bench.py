@@ -350,6 +350,31 @@ def ring_overlap(wl, cp, torch, steps, ms_plain):
             "xgmi_link_ms_per_ring_step_bwd": round((kv_b + grad_b) / (XGMI_LINK_GBS * 1e9) * 1e3, 4)}
 
 
+def allgather_share(wl, cp, torch, steps, ms_ring):
+    """The same rank's share under all-gather context parallelism
+    (cp_allgather_share): its two query runs against the whole gathered
+    sequence in one forward and one backward call -- the same causal pairs as
+    its ring share.  K/V here are random rows, so their order does not matter
+    for the timing."""
+    ws = cp.workspace(cp.cp_allgather_workspace_bytes(wl.sh, wl.S, wl.P, False, True))
+
+    def run():
+        cp.cp_allgather_share(wl.sh, wl.S, wl.P, 0, wl.q, wl.k, wl.v, None, wl.o, wl.lse, wl.dout, wl.dq,
+                              wl.dk, wl.dv, workspace=ws)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = wl.flops_fwd + wl.flops_bwd
+    return {"ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "vs_ring_step": round(ms / ms_ring, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -445,6 +470,8 @@ def main():
         out["ring_balance"] = bal
     if wl.name in ("ring_128k", "usp_1m"):
         out["ring_overlap"] = ring_overlap(wl, cp, torch, max(1, min(args.steps, 3)), ms)
+    if wl.name == "ring_128k":
+        out["allgather_share"] = allgather_share(wl, cp, torch, max(1, min(args.steps, 3)), ms)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
