@@ -161,11 +161,10 @@ __device__ inline float fwd_accumulate(FwdState<D>& st, const TrReader<D>& tr, u
 }
 
 // ---- software-pipelined tile (full tiles, reference point set) -------------
-// Per 64-key tile: S0 = QK(keys 0..31); then S1 = QK(keys 32..63) interleaved
-// with exp(S0); then O += V0 P0 interleaved with exp(S1); then O += V1 P1.
-// The interleaving (1 MFMA, then VALU work, repeated) lets the VALU softmax run
-// while the matrix core executes the independent MFMAs; it is imposed with
-// sched_group_barrier because the scheduler would otherwise cluster them.
+// Per 64-key tile: S0 = QK(keys 0..31); then S1 = QK(keys 32..63) beside
+// exp(S0); then O += V0 P0 beside exp(S1); then O += V1 P1.  The stages are
+// independent, so the compiler interleaves each stage's MFMAs with the other
+// half's softmax VALU work; the second wave on the SIMD fills what remains.
 
 template <int D>
 __device__ inline void qk_half(const FwdState<D>& st, const RowReader<D>& rr, uint32_t Kt, int kb, f32x16 (&s)[NQB]) {

@@ -226,33 +226,6 @@ struct TrReader {
   }
 };
 
-// ---- instruction-scheduling helpers ----------------------------------------
-// Interleave n MFMAs with v VALU instructions after each (sched_group_barrier
-// masks: 0x008 MFMA, 0x002 VALU).  Used where a stage's MFMAs are independent
-// of the VALU work placed next to them, so the VALU runs while the matrix core
-// is busy; without it the scheduler clusters the two kinds.
-#define CP_INTERLEAVE(n, v)                                   \
-  do {                                                        \
-    _Pragma("unroll") for (int i_ = 0; i_ < (n); ++i_) {      \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      \
-      __builtin_amdgcn_sched_group_barrier(0x002, (v), 0);    \
-    }                                                         \
-  } while (0)
-
-// The same with the stage's LDS reads placed too: `lead` reads first, then
-// after each MFMA its v VALU instructions and d more reads (0x100: DS read).
-// Reads are thereby requested a fixed distance ahead of the MFMAs that use
-// them instead of just before.
-#define CP_PIPE(lead, n, v, d)                                \
-  do {                                                        \
-    __builtin_amdgcn_sched_group_barrier(0x100, (lead), 0);   \
-    _Pragma("unroll") for (int i_ = 0; i_ < (n); ++i_) {      \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      \
-      __builtin_amdgcn_sched_group_barrier(0x002, (v), 0);    \
-      __builtin_amdgcn_sched_group_barrier(0x100, (d), 0);    \
-    }                                                         \
-  } while (0)
-
 // Pin values in place: an empty asm that reads them, so the compiler cannot
 // sink their computation into a later block (which would undo an
 // interleaving above it).
