@@ -211,3 +211,43 @@ def test_ring_overlap_matches_plain_bitwise(gpu_lib, docs):
             torch.cuda.synchronize()
             for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), got, ref):
                 assert torch.equal(a, b), f"rank {r} call {call}: {name} differs"
+
+
+def test_usp_mini_full(gpu_lib):
+    """The USP structure (Ulysses 4 x ring 4) at S=8,192: the Ulysses rank-2
+    head slice of a 16/4-head layer (4 query heads, 1 KV head, read in place
+    through the strides) driven through the zigzag ring over all 4 ring
+    ranks, checked in full against the oracle's attention over that slice --
+    O, LSE, dQ and the complete dK, dV."""
+    S, P, HQ, HKV, d, sp, u = 8192, 4, 16, 4, 128, 4, 2
+    dtype = torch.bfloat16
+    (h0, h1), (g0, g1) = Z.head_slice(HQ, HKV, sp, u)
+    hq, hkv = h1 - h0, g1 - g0
+    print(f"usp mini: heads {h0}:{h1}, kv {g0}:{g1}", flush=True)
+    (qh, kh, vh), (qd, kd, vd) = inputs(41, [(S, HQ, d), (S, HKV, d), (S, HKV, d)], dtype)
+    (doh,), (dod,) = inputs(42, [(S, hq, d)], dtype)
+    order = Z.sharded_order(S, P)                         # global rows in sharded order
+    order_d = torch.as_tensor(order, device=DEV)
+    qs_d, ks_d, vs_d, dos_d = qd[order_d], kd[order_d], vd[order_d], dod[order_d]
+    sh = cp.make_shape(hq, hkv, d, HQ * d, HKV * d, 1.0 / np.sqrt(d), True, cp.CP_BF16)
+    n = S // P
+    o = torch.empty(S, hq, d, device=DEV, dtype=dtype)
+    lse = torch.empty(P, hq, n, device=DEV)
+    dq = torch.empty(S, hq, d, device=DEV)
+    dk = torch.empty(S, hkv, d, device=DEV)
+    dv = torch.empty_like(dk)
+    ws = cp.workspace(cp.cp_ring_workspace_bytes(sh, S, P, -1, cp.CP_BF16, True))
+    cp.cp_ring_emulate(sh, S, P, -1, qs_d[:, h0:h1], ks_d[:, g0:g1], vs_d[:, g0:g1], None, o, lse, dos_d,
+                       dq, dk, dv, workspace=ws)
+    torch.cuda.synchronize()
+    pos = np.arange(S)
+    q1, k1, v1 = qh[:, h0:h1], kh[:, g0:g1], vh[:, g0:g1]
+    ro, rl = A.forward(q1, k1, v1, pos, pos, scale=sh.scale, causal=True)
+    rdq, rdk, rdv = A.backward(q1, k1, v1, doh, rl, A.delta(ro, doh), pos, pos, scale=sh.scale, causal=True)
+    tol = TOL[dtype]
+    assert max_abs(host(o), ro[order]) <= tol["o"]
+    gl = host(lse).transpose(1, 0, 2).reshape(hq, S)
+    assert lse_err(gl, rl[:, order]) <= tol["lse"]
+    assert max_abs(host(dq), rdq[order]) <= grad_tol(rdq, tol["grad"])
+    assert max_abs(host(dk), rdk[order]) <= grad_tol(rdk, tol["grad"])
+    assert max_abs(host(dv), rdv[order]) <= grad_tol(rdv, tol["grad"])
