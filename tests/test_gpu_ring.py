@@ -177,19 +177,23 @@ def test_allgather_share_one_rank(gpu_lib, dtype, docs):
     assert max_abs(host(dv), rdv) <= grad_tol(rdv, tol["grad"])
 
 
-@pytest.mark.parametrize("docs", [False, True], ids=["causal", "docs"])
-def test_ring_overlap_matches_plain_bitwise(gpu_lib, docs):
+@pytest.mark.parametrize("dtype,P,docs", [(torch.bfloat16, 4, False), (torch.bfloat16, 4, True),
+                                          (torch.float32, 4, False), (torch.bfloat16, 2, True),
+                                          (torch.bfloat16, 1, False)],
+                         ids=["bf16-P4", "bf16-P4-docs", "f32-P4", "bf16-P2-docs", "bf16-P1"])
+def test_ring_overlap_matches_plain_bitwise(gpu_lib, dtype, P, docs):
     """The traffic emulation only moves where each step's KV shard is read
     from (a receive area filled on a second stream), so its outputs equal the
     plain driver's bit for bit; K/V are head slices of a wider layer, so the
-    receive copy is a strided one.  Two calls in a row reuse the workspace."""
-    S, P, hq, hkv, d = 1024, 4, 4, 2, 128
-    dtype = torch.bfloat16
-    print(f"ring overlap docs={docs}", flush=True)
+    receive copy is a strided one.  Two calls in a row reuse the workspace.
+    P = 1 has no transfers; P = 2 uses one of the two receive buffers."""
+    S, hq, hkv, d = 1024, 4, 2, 128
+    print(f"ring overlap {dtype} P={P} docs={docs}", flush=True)
     (_, _, _, _), (qd, kw, vw, dod), doc = _ring_inputs(S, P, hq, 2 * hkv, d, dtype, 21, docs)
     kd, vd = kw[:, hkv:], vw[:, hkv:]                    # the second half of the layer's KV heads
     doc_d = None if doc is None else torch.from_numpy(doc).to(DEV)
-    sh = cp.make_shape(hq, hkv, d, hq * d, 2 * hkv * d, 1.0 / np.sqrt(d), True, cp.CP_BF16)
+    sh = cp.make_shape(hq, hkv, d, hq * d, 2 * hkv * d, 1.0 / np.sqrt(d), True,
+                       cp.CP_BF16 if dtype == torch.bfloat16 else cp.CP_F32)
     n = S // P
     side = torch.cuda.Stream()
 
