@@ -214,15 +214,16 @@ __device__ inline void unpark_add(uint32_t P, f32x16 (&acc)[D / 32], int lane) {
     }
 }
 
-// dst[key row, d] += mul * acc (accumulator layout: d = db*32 + 8j + 4hh + i)
+// dst[key row, d] += mul * acc, or = with `store` (accumulator layout:
+// d = db*32 + 8j + 4hh + i)
 template <int D>
-__device__ inline void add_rows(float* dst, const f32x16 (&acc)[D / 32], float mul, int hh) {
+__device__ inline void add_rows(float* dst, const f32x16 (&acc)[D / 32], float mul, int hh, bool store) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       f32x4* p = (f32x4*)(dst + db * 32 + j * 8 + hh * 4);
-      f32x4 o = *p;
+      f32x4 o = store ? f32x4{} : *p;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] += mul * acc[db][4 * j + i];
       *p = o;
@@ -388,14 +389,14 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
   __syncthreads();
   if (qh == 0) {
     unpark_add<D>(P, st.dka, lane);
-    if (writer) add_rows<D>(krow, st.dka, a.scale, hh);
+    if (writer) add_rows<D>(krow, st.dka, a.scale, hh, a.store != 0);
   }
   __syncthreads();
   if (qh == 0) park_acc<D>(P, st.dva, lane);
   __syncthreads();
   if (qh == 1) {
     unpark_add<D>(P, st.dva, lane);
-    if (writer) add_rows<D>(vrow, st.dva, 1.0f, hh);
+    if (writer) add_rows<D>(vrow, st.dva, 1.0f, hh, a.store != 0);
   }
 }
 
@@ -613,7 +614,7 @@ __global__ __launch_bounds__(64 * DNW, 1) void dq_bf16_kernel(BwdParams a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           f32x4* p = (f32x4*)(dst + db * 32 + j * 8 + hh * 4);
-          f32x4 v = *p;
+          f32x4 v = a.store ? f32x4{} : *p;
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] += a.scale * st.acc[qb][db][4 * j + i];
           *p = v;

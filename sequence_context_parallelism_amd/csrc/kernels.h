@@ -47,9 +47,10 @@ struct BwdParams {
   const float* lse;          // final LSE   [hq, lse_ld]
   const float* delta;        // final Delta [hq, lse_ld]
   int64_t lse_ld;
-  float* dq;                 // [Lq, hq, d]  +=
-  float* dk;                 // [Lk, hkv, d] +=
-  float* dv;                 // [Lk, hkv, d] +=
+  float* dq;                 // [Lq, hq, d]  += (or = with store)
+  float* dk;                 // [Lk, hkv, d] += (or = with store)
+  float* dv;                 // [Lk, hkv, d] += (or = with store)
+  int store;                 // bf16 path: 1 = write the gradients (the call's pairs are all of them), 0 = add
   // filled in by the launcher
   int nkt, n_work;
   int heads_per_wg, qblocks_per_wg, nqt;

@@ -123,11 +123,12 @@ def test_ulysses_share_is_head_slice(gpu_lib, dtype):
     for r in range(sp):
         hs, gs = hq // sp, hkv // sp
         (_, dosh), (_, dosd) = inputs(33 + r, [(1,), (S, hs, d)], dtype)
-        o = torch.empty(S, hs, d, device=DEV, dtype=dtype)
-        lse = torch.empty(hs, S, device=DEV)
-        dq = torch.empty(S, hs, d, device=DEV)
-        dk = torch.empty(S, gs, d, device=DEV)
-        dv = torch.empty_like(dk)
+        nan = float("nan")   # outputs start as NaN: every row must be written
+        o = torch.full((S, hs, d), nan, device=DEV, dtype=dtype)
+        lse = torch.full((hs, S), nan, device=DEV)
+        dq = torch.full((S, hs, d), nan, device=DEV)
+        dk = torch.full((S, gs, d), nan, device=DEV)
+        dv = torch.full_like(dk, nan)
         ws = cp.workspace(cp.cp_ulysses_workspace_bytes(sh, S, sp, True))
         cp.cp_ulysses_share(sh, S, sp, r, qd, kd, vd, None, o, lse, dosd, dq, dk, dv, workspace=ws)
         torch.cuda.synchronize()
@@ -159,11 +160,12 @@ def test_allgather_share_one_rank(gpu_lib, dtype, docs):
     n = S // P
     q_r = qd[torch.as_tensor(rows, device=DEV)].contiguous()
     do_r = dod[torch.as_tensor(rows, device=DEV)].contiguous()
-    o = torch.empty(n, hq, d, device=DEV, dtype=dtype)
-    lse = torch.empty(hq, n, device=DEV)
-    dq = torch.empty(n, hq, d, device=DEV)
-    dk = torch.empty(S, hkv, d, device=DEV)
-    dv = torch.empty_like(dk)
+    nan = float("nan")   # outputs start as NaN: every row must be written
+    o = torch.full((n, hq, d), nan, device=DEV, dtype=dtype)
+    lse = torch.full((hq, n), nan, device=DEV)
+    dq = torch.full((n, hq, d), nan, device=DEV)
+    dk = torch.full((S, hkv, d), nan, device=DEV)
+    dv = torch.full_like(dk, nan)
     doc_d = None if doc is None else torch.from_numpy(doc).to(DEV)
     ws = cp.workspace(cp.cp_allgather_workspace_bytes(sh, S, P, docs, True))
     cp.cp_allgather_share(sh, S, P, r, q_r, kd, vd, doc_d, o, lse, do_r, dq, dk, dv, workspace=ws)
