@@ -236,9 +236,9 @@ template <int D>
 __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
   // LDS arena: Q and dO tiles (double-buffered), then per-row LSE (as
   // -LSE log2 e), -Delta and doc ids, each double-buffered, then the work-
-  // group's V rows (read as MFMA B operands).  After the tile loop the tile
-  // area holds the parked partial accumulators (4 x 32 keys x D floats = as
-  // many bytes as the four tiles).
+  // group's V rows and K rows (read as MFMA B operands).  After the tile loop
+  // the tile area holds the parked partial accumulators (4 x 32 keys x D
+  // floats = as many bytes as the four tiles).
   constexpr uint32_t TB = BQ * D * 2, RW = BQ * 4;
   constexpr uint32_t Q0 = 0, Q1 = TB, O0 = 2 * TB, O1 = 3 * TB;
   constexpr uint32_t L0 = 4 * TB, L1 = L0 + RW, N0 = L1 + RW, N1 = N0 + RW, X0 = N1 + RW, X1 = X0 + RW;
