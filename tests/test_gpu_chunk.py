@@ -23,6 +23,7 @@ CASES = [
     ("three_kv_heads", 12, 3, 64, (0, 150), (0, 150), True, False),     # groups not dividing 8
     ("sixteen_kv_heads", 64, 16, 64, (0, 70), (0, 70), True, False),    # groups a multiple of 8
     ("tiny_5x7", 4, 2, 128, (2, 5), (0, 7), True, False),               # one partial tile each way
+    ("mqa_g16", 16, 1, 128, (0, 150), (0, 150), True, False),           # 16 query heads on one KV head
     ("one_row_half_one_key_block", 4, 1, 128, (0, 33), (0, 129), False, False),   # 2nd query half: 1 row
 ]
 

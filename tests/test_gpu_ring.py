@@ -257,3 +257,30 @@ def test_usp_mini_full(gpu_lib):
     assert max_abs(host(dq), rdq[order]) <= grad_tol(rdq, tol["grad"])
     assert max_abs(host(dk), rdk[order]) <= grad_tol(rdk, tol["grad"])
     assert max_abs(host(dv), rdv[order]) <= grad_tol(rdv, tol["grad"])
+
+
+def test_ring_single_rank_is_plain_causal_attention(gpu_lib):
+    """P = 1: one rank holds chunks 0 and 1, i.e. the whole sequence in order,
+    and its one step is plain causal attention (forward and backward)."""
+    S, P, hq, hkv, d = 512, 1, 4, 2, 128
+    dtype = torch.bfloat16
+    (qh, kh, vh, doh), (qd, kd, vd, dod), _ = _ring_inputs(S, P, hq, hkv, d, dtype, 5)
+    sh = shape_for(hq, hkv, d, dtype)
+    nan = float("nan")
+    o = torch.full((S, hq, d), nan, device=DEV, dtype=dtype)
+    lse = torch.full((hq, S), nan, device=DEV)
+    dq = torch.full((S, hq, d), nan, device=DEV)
+    dk = torch.full((S, hkv, d), nan, device=DEV)
+    dv = torch.full_like(dk, nan)
+    ws = cp.workspace(cp.cp_ring_workspace_bytes(sh, S, P, 0, sh.dtype, True))
+    cp.cp_ring_emulate(sh, S, P, 0, qd, kd, vd, None, o, lse, dod, dq, dk, dv, workspace=ws)
+    torch.cuda.synchronize()
+    pos = np.arange(S)
+    ro, rl = A.forward(qh, kh, vh, pos, pos, scale=sh.scale, causal=True)
+    rdq, rdk, rdv = A.backward(qh, kh, vh, doh, rl, A.delta(ro, doh), pos, pos, scale=sh.scale, causal=True)
+    tol = TOL[dtype]
+    assert max_abs(host(o), ro) <= tol["o"]
+    assert lse_err(host(lse), rl) <= tol["lse"]
+    assert max_abs(host(dq), rdq) <= grad_tol(rdq, tol["grad"])
+    assert max_abs(host(dk), rdk) <= grad_tol(rdk, tol["grad"])
+    assert max_abs(host(dv), rdv) <= grad_tol(rdv, tol["grad"])
