@@ -305,12 +305,27 @@ def cpu_baseline(wl):
     o, lse = A.forward(q, k, v, pos, pos, scale=scale, causal=True)
     A.backward(q, k, v, do, lse, A.delta(o, do), pos, pos, scale=scale, causal=True)
     t = time.perf_counter() - t0
-    flops = 14 * wl.d * (L * (L + 1) // 2) * g
+    pairs = (L * (L + 1) // 2) * g
+    flops = 14 * wl.d * pairs
     cores = len(os.sched_getaffinity(0))
+    try:   # the threads the BLAS behind numpy actually ran with
+        import threadpoolctl
+        blas = [p["num_threads"] for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+        if blas:
+            cores = min(cores, max(blas))
+    except Exception:
+        pass
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": flops / t / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
             "sample": f"fp64 numpy oracle, forward+backward of one KV group ({g} query heads) over the "
                       f"first {L} tokens, causal; {t:.1f} s",
-            "seconds": t, "torch_threads": torch.get_num_threads()}
+            "seconds": t, "pairs_per_s": pairs / t, "gflops_fp64": flops / t / 1e9, "cpu_model": model,
+            "torch_threads": torch.get_num_threads()}
 
 
 XGMI_LINK_GBS = 153.0   # one xGMI link, per direction (the ring's neighbour link)
