@@ -104,14 +104,23 @@ hipError_t run_fwd(const cp_shape* sh, const void* q, const cp_span& qs, const v
 
 enum BwdPart { BWD_ALL, BWD_DKDV, BWD_DQ };
 
-// With `store` (bf16 only) the kernels write the gradients instead of adding
-// to them: for a call whose pairs are all the pairs of these rows, so the
-// outputs need no zero-fill first.
+// With `store` the gradients are written instead of added to: for a call
+// whose pairs are all the pairs of these rows.  The bf16 kernels store
+// directly (no zero-fill, no read of the old values); for fp32 the outputs
+// are zero-filled and the kernels accumulate.
 hipError_t run_bwd(const cp_shape* sh, const void* q, const cp_span& qs, const void* k, const void* v,
                    const cp_span& ks, const void* dout, const float* lse, const float* delta,
                    int64_t lse_ld, float* dq, float* dk, float* dv, hipStream_t st, BwdPart part = BWD_ALL,
                    bool store = false) {
   const int64_t Lq = (int64_t)qs.len[0] + qs.len[1], Lk = (int64_t)ks.len[0] + ks.len[1];
+  if (store && sh->dtype == CP_F32) {    // the fp32 kernels only accumulate: zero the outputs first
+    hipError_t e = hipSuccess;
+    if (part != BWD_DKDV) e = launch_fill_zero(Lq * sh->hq * sh->d, dq, st);
+    if (e == hipSuccess && part != BWD_DQ) e = launch_fill_zero(Lk * sh->hkv * sh->d, dk, st);
+    if (e == hipSuccess && part != BWD_DQ) e = launch_fill_zero(Lk * sh->hkv * sh->d, dv, st);
+    if (e != hipSuccess) return e;
+    store = false;
+  }
   if (store && (Lq == 0 || Lk == 0)) {   // no pairs: the written gradients are zeros
     hipError_t e = hipSuccess;
     if (Lk == 0 && part != BWD_DKDV) e = launch_fill_zero(Lq * sh->hq * sh->d, dq, st);
@@ -622,18 +631,11 @@ cp_status cp_ulysses_share(const cp_shape* sh_full, int64_t S, int32_t sp, int32
   CP_TRY_HIP(run_fwd(&sh, qs_ptr, span, ks_ptr, vs_ptr, span, o, o_dtype, lse, S, st), "ulysses forward");
   if (backward) {
     float* dlt = (float*)workspace;
-    const int64_t orow = (int64_t)sh.hq * sh.d, kvrow = (int64_t)sh.hkv * sh.d;
-    // one chunk holds every pair: the bf16 kernels write the gradients
-    // directly; the fp32 path accumulates into zeroed outputs
-    const bool store = sh.dtype == CP_BF16;
-    if (!store) {
-      CP_TRY_HIP(launch_fill_zero(S * orow, dq, st), "zero dq");
-      CP_TRY_HIP(launch_fill_zero(S * kvrow, dk, st), "zero dk");
-      CP_TRY_HIP(launch_fill_zero(S * kvrow, dv, st), "zero dv");
-    }
+    // one chunk holds every pair: the gradients are written, not added to
+    // (run_bwd zero-fills first where the kernels only accumulate)
     CP_TRY_HIP(launch_delta(S, sh.hq, sh.d, o, o_dtype == CP_F32, dout, sh.dtype == CP_F32, dlt, S, st),
                "ulysses delta");
-    CP_TRY_HIP(run_bwd(&sh, qs_ptr, span, ks_ptr, vs_ptr, span, dout, lse, dlt, S, dq, dk, dv, st, BWD_ALL, store),
+    CP_TRY_HIP(run_bwd(&sh, qs_ptr, span, ks_ptr, vs_ptr, span, dout, lse, dlt, S, dq, dk, dv, st, BWD_ALL, true),
                "ulysses backward");
   }
   return ok();
@@ -729,16 +731,10 @@ cp_status cp_allgather_share(const cp_shape* sh, int64_t S, int32_t P, int32_t r
   const cp_span ks = run_span(0, (int32_t)S, S, 0, doc);
   CP_TRY_HIP(run_fwd(sh, q, qs, k, v, ks, o, o_dtype, lse, n, st), "all-gather forward");
   if (backward) {
-    const int64_t orow = (int64_t)sh->hq * sh->d, kvrow = (int64_t)sh->hkv * sh->d;
-    const bool store = sh->dtype == CP_BF16;   // one call holds every pair (see cp_ulysses_share)
-    if (!store) {
-      CP_TRY_HIP(launch_fill_zero(n * orow, dq, st), "zero dq");
-      CP_TRY_HIP(launch_fill_zero(S * kvrow, dk, st), "zero dk");
-      CP_TRY_HIP(launch_fill_zero(S * kvrow, dv, st), "zero dv");
-    }
+    // one call holds every pair: the gradients are written (see cp_ulysses_share)
     CP_TRY_HIP(launch_delta(n, sh->hq, sh->d, o, o_dtype == CP_F32, dout, sh->dtype == CP_F32, dlt, n, st),
                "all-gather delta");
-    CP_TRY_HIP(run_bwd(sh, q, qs, k, v, ks, dout, lse, dlt, n, dq, dk, dv, st, BWD_ALL, store),
+    CP_TRY_HIP(run_bwd(sh, q, qs, k, v, ks, dout, lse, dlt, n, dq, dk, dv, st, BWD_ALL, true),
                "all-gather backward");
   }
   return ok();
