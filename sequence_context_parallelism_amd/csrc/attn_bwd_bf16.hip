@@ -297,11 +297,11 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
     }
     const int32_t row = min(qt * BQ + lane, Lq - 1);
     if (wave == 0)
-      __builtin_amdgcn_global_load_lds((const void*)(a.lse + (int64_t)head * a.lse_ld + row), CP_LDS_AT(Ld), 4, 0, 0);
+      row_load_lds(a.lse + (int64_t)head * a.lse_ld, row, Ld);
     else if (wave == 1)
-      __builtin_amdgcn_global_load_lds((const void*)(a.delta + (int64_t)head * a.lse_ld + row), CP_LDS_AT(Dd), 4, 0, 0);
+      row_load_lds(a.delta + (int64_t)head * a.lse_ld, row, Dd);
     else if (wave == 2 && docs)
-      __builtin_amdgcn_global_load_lds((const void*)(qs.doc + row), CP_LDS_AT(Xd), 4, 0, 0);
+      row_load_lds(qs.doc, row, Xd);
   };
   auto prepare = [&](uint32_t Ld, uint32_t Dd) {
     if (wave == 0) lds_stf(Ld + 4 * lane, neg_lse2(lds_ldf(Ld + 4 * lane)));
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(64 * DNW, 1) void dq_bf16_kernel(BwdParams a) {
     }
     if (docs && wave == 0) {
       const int32_t row = min(t * BK + lane, Lk - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(ks.doc + row), CP_LDS_AT(Xd), 4, 0, 0);
+      row_load_lds(ks.doc, row, Xd);
     }
   };
   if (kt0 < kt1) issue(kt0, S0 + K0, S0 + V0, S0 + X0);

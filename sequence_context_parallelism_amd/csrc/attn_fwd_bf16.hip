@@ -358,7 +358,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void fwd_bf16_kernel(FwdParams a) {
     }
     if (docs && wave == 0) {
       const int32_t row = min(kt * BK + lane, Lk - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(ks.doc + row), CP_LDS_AT(Dd), 4, 0, 0);
+      row_load_lds(ks.doc, row, Dd);
     }
   };
   if (kt0 < kt1) issue(kt0, S0 + K0, S0 + V0, S0 + X0);

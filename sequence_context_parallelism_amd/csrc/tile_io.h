@@ -1,7 +1,7 @@
 // LDS tile staging shared by the bf16 MFMA kernels (gfx950).
 //
 // A tile of R rows x D bf16 (row-major in HBM, `stride` elements between
-// rows) is copied HBM -> LDS with direct-to-LDS loads (global_load_lds,
+// rows) is copied HBM -> LDS with direct-to-LDS loads (buffer_load ... lds,
 // 16 bytes per lane; no VGPR round trip).  The LDS image keeps rows whole but
 // permutes each row's 16-byte chunks by an XOR swizzle so that both access
 // patterns the MFMA operands need are free of bank conflicts:
@@ -51,35 +51,29 @@ struct Swz {
   }
 };
 
-// Issue the direct-to-LDS loads of an R x D tile whose row i sits at
-// src + row_index(i) * stride (rows past `valid` are clamped to valid-1, so
-// every load is in bounds; callers mask those rows).  NW waves share the
-// work; wave `wave` issues its share.  dst must be 16-byte aligned.
-template <int D, int R, int NW>
-__device__ inline void tile_load_lds(char* dst, const __bf16* src, int64_t stride, int32_t row0,
-                                     int32_t valid_rows, int wave, int lane) {
-  constexpr int CHUNKS = D / 8;
-  constexpr int TOTAL = R * CHUNKS;                  // 16-byte chunks in the tile
-  constexpr int PER_WAVE = TOTAL / (64 * NW);        // instructions per wave
-  static_assert(TOTAL % (64 * NW) == 0, "tile must split evenly over the waves");
-#pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int slot0 = (wave * PER_WAVE + i) * 64;   // first LDS slot of this instruction
-    const int slot = slot0 + lane;
-    const int r = slot / CHUNKS;
-    const int cpos = slot % CHUNKS;
-    int c = cpos;   // invert the swizzle: the chunk stored at position cpos
-    if constexpr (D == 128) c = cpos ^ (((r & 3) << 2) | ((r >> 2) & 3));
-    else c = cpos ^ ((r >> 1) & 7);
-    int32_t row = row0 + r;
-    row = row < valid_rows ? row : valid_rows - 1;
-    const __bf16* g = src + (int64_t)row * stride + c * 8;
-    __builtin_amdgcn_global_load_lds((const void*)g, CP_LDS_PTR(dst + slot0 * 16), 16, 0, 0);
-  }
+// Direct-to-LDS loads are issued as buffer loads (buffer_load ... lds)
+// through a raw buffer resource on a wave-uniform base, with a per-lane byte
+// offset, rather than as global_load_lds: while a global_load_lds is in
+// flight the compiler treats LDS completions as unordered and waits for
+// every outstanding LDS read at each use, which defeats register
+// prefetching of MFMA operands; with buffer loads it keeps exact counts.
+__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+// 16 bytes per lane at base + voff into LDS [lds + 16 lane, +16)
+__device__ inline void buf_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, CP_LDS_AT(lds), 16, voff, 0, 0, 0);
+}
+// One 4-byte element per lane: element `idx` of the array at `base` into LDS
+// [lds + 4 lane, +4).
+__device__ inline void row_load_lds(const void* base, int32_t idx, uint32_t lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(base), CP_LDS_AT(lds), 4, (uint32_t)idx * 4u, 0, 0, 0);
 }
 
-// The same for a tile at LDS address `dst` (a compile-time offset in the
-// kernel's LDS arena).
+// Issue the direct-to-LDS loads of an R x D tile at LDS address `dst` whose
+// row i sits at src + i * stride (rows past `valid_rows` are clamped to
+// valid_rows - 1, so every load is in bounds; callers mask those rows).  NW
+// waves share the work; wave `wave` issues its share.
 template <int D, int R, int NW>
 __device__ inline void tile_load_lds(uint32_t dst, const __bf16* src, int64_t stride, int32_t row0,
                                      int32_t valid_rows, int wave, int lane) {
@@ -87,6 +81,7 @@ __device__ inline void tile_load_lds(uint32_t dst, const __bf16* src, int64_t st
   constexpr int TOTAL = R * CHUNKS;
   constexpr int PER_WAVE = TOTAL / (64 * NW);
   static_assert(TOTAL % (64 * NW) == 0, "tile must split evenly over the waves");
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(src + (int64_t)row0 * stride);
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int slot0 = (wave * PER_WAVE + i) * 64;
@@ -98,9 +93,7 @@ __device__ inline void tile_load_lds(uint32_t dst, const __bf16* src, int64_t st
     else c = cpos ^ ((r >> 1) & 7);
     int32_t row = row0 + r;
     row = row < valid_rows ? row : valid_rows - 1;
-    const __bf16* g = src + (int64_t)row * stride + c * 8;
-    __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + slot0 * 16),
-                                     16, 0, 0);
+    buf_lds16(rs, dst + slot0 * 16, (uint32_t)((row - row0) * stride * 2 + c * 16));
   }
 }
 
@@ -129,10 +122,9 @@ struct TileLoader {
   }
   // tile rows start at byte address `src` (wave-uniform); LDS tile at `dst`
   __device__ inline void load(uint32_t dst, const char* src) const {
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(src);
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(src + off[i]),
-                                       CP_LDS_AT(dst + (uint32_t)((wave * PER_WAVE + i) * 1024)), 16, 0, 0);
+    for (int i = 0; i < PER_WAVE; ++i) buf_lds16(rs, dst + (uint32_t)((wave * PER_WAVE + i) * 1024), off[i]);
   }
 };
 
