@@ -101,7 +101,10 @@ __device__ inline void dkdv_mask(const KvState<D>& st, f32x16& s, uint32_t QDt, 
 //
 // Explicit software pipeline (scheduling walls keep the order): operand
 // reads run two MFMAs ahead through a two-entry register ring, and slot 1's
-// P/dS VALU work is spread over slot 0's gradient MFMAs.
+// P/dS VALU work is spread over slot 0's gradient MFMAs.  The wave raises its
+// issue priority for its two MFMA stretches and drops it for the mask and
+// slot 0's P/dS, so the SIMD's other wave, if it is in a VALU stretch, yields
+// the issue slots to the MFMAs, and its own VALU work fills the gaps.
 template <int D>
 __device__ inline void dkdv_block(KvState<D>& st, const RowReader<D>& rq, const TrReader<D>& tq, uint32_t Qt,
                                   uint32_t Ot, uint32_t vb, uint32_t Nl, uint32_t NDt, uint32_t QDt, int32_t qa0,
@@ -118,6 +121,7 @@ __device__ inline void dkdv_block(KvState<D>& st, const RowReader<D>& rq, const 
       for (int i = 0; i < 4; ++i) init[j * 4 + i] = d4[i];
     }
     bf16x8 ra[2], ro[2], rv[2], rk[2];
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       ra[k] = rq.at(Qt, 0, k);
@@ -139,6 +143,7 @@ __device__ inline void dkdv_block(KvState<D>& st, const RowReader<D>& rq, const 
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   if (mask) dkdv_mask<D>(st, s, QDt, qa0, qb, Lq, docs, hh);
   __builtin_amdgcn_sched_barrier(0);
 
@@ -166,6 +171,7 @@ __device__ inline void dkdv_block(KvState<D>& st, const RowReader<D>& rq, const 
   const f32x4 n2 = lds_f4(Nl + 4 * (qb * 32 + 2 * 8 + hh * 4));
   const f32x4 n3 = lds_f4(Nl + 4 * (qb * 32 + 3 * 8 + hh * 4));
   __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
   constexpr int PER = 8 / NDB;   // slot-1 elements per slot-0 MFMA pair
 #pragma unroll
   for (int m = 0; m < 2 * NDB; ++m) {
@@ -185,6 +191,7 @@ __device__ inline void dkdv_block(KvState<D>& st, const RowReader<D>& rq, const 
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 __device__ inline void lds_st4(uint32_t a, const f32x4& x) {
