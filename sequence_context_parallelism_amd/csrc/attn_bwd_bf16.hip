@@ -424,80 +424,87 @@ struct QState {
   int32_t qdoc[DQB];
 };
 
-// S^T and dP^T of the 32-key half kb.  Element r of block qb: query = the
-// lane's column of block qb, key = kb*32 + 8(r/4) + 4hh + r%4.
+// S^T accumulator element r of the 32-key half starting at key kh0 of the
+// tile: query = the lane's column, key = kh0 + 8(r/4) + 4hh + r%4.  Masked
+// entries get -inf.
 template <int D>
-__device__ inline void sdp_half(const QState<D>& st, const RowReader<D>& rr, uint32_t Kt, uint32_t Vt, int kb,
-                                f32x16 (&s)[DQB], f32x16 (&dp)[DQB]) {
-#pragma unroll
-  for (int kd = 0; kd < D / 16; ++kd) {
-    const bf16x8 ka = rr.at(Kt, kb, kd), va = rr.at(Vt, kb, kd);
-#pragma unroll
-    for (int qb = 0; qb < DQB; ++qb) {
-      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qf[qb][kd], kd ? s[qb] : f32x16{}, 0, 0, 0);
-      dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, st.of[qb][kd], kd ? dp[qb] : f32x16{}, 0, 0, 0);
-    }
-  }
-}
-
-template <int D>
-__device__ inline void dq_mask(const QState<D>& st, f32x16 (&s)[DQB], uint32_t Dt, int32_t kb0, int kh0, bool docs,
+__device__ inline void dq_mask(const QState<D>& st, f32x16& s, uint32_t Dt, int32_t kb0, int kh0, bool docs,
                                int hh) {
   asm volatile("; partial tile" ::: "memory");   // keeps the caller's branch real (no if-conversion)
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int kk = kh0 + (r >> 2) * 8 + hh * 4 + (r & 3);
     const int32_t kd_ = lds_ld4i(Dt + 4 * kk);
-#pragma unroll
-    for (int qb = 0; qb < DQB; ++qb) {
-      const bool ok = (kb0 + kk < st.lim[qb]) & (!docs | (kd_ == st.qdoc[qb]));
-      s[qb][r] = ok ? s[qb][r] : -INFINITY;
-    }
+    const bool ok = (kb0 + kk < st.lim[0]) & (!docs | (kd_ == st.qdoc[0]));
+    s[r] = ok ? s[r] : -INFINITY;
   }
 }
 
-template <int D>
-__device__ inline void ds_half(const QState<D>& st, const f32x16 (&s)[DQB], const f32x16 (&dp)[DQB], float c,
-                               bf16x8 (&dsf)[DQB][2]) {
-#pragma unroll
-  for (int qb = 0; qb < DQB; ++qb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, st.nl[qb]));
-      dsf[qb][r >> 3][r & 7] = (__bf16)(p * (dp[qb][r] - st.dl[qb]));
-    }
-}
-
-// dQ^T[qb][db] += K^T (d rows, 16 keys per step) x dS^T for the half kb
-template <int D>
-__device__ inline void dq_half(QState<D>& st, const TrReader<D>& tr, uint32_t Kt, int kb, const bf16x8 (&dsf)[DQB][2]) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const bf16x8 ka = tr.at(Kt, kb * 32 + 16 * t, db);
-#pragma unroll
-      for (int qb = 0; qb < DQB; ++qb)
-        st.acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsf[qb][t], st.acc[qb][db], 0, 0, 0);
-    }
-}
-
+// One 64-key tile for one wave as an explicit software pipeline (scheduling
+// walls keep the order): S^T, dP^T of key half 0; those of half 1 beside
+// half 0's dS^T; dQ^T += K^T dS^T of half 0 beside half 1's dS^T; then half
+// 1's.  Operand reads run two MFMAs ahead through two-entry register rings.
+// dS^T = P^T (dP^T - Delta) with P^T = exp2(S^T c + nl) goes from the
+// accumulator layout straight into the B operand of the dQ^T product.
 template <int D>
 __device__ inline void dq_tile(QState<D>& st, const RowReader<D>& rr, const TrReader<D>& tr, uint32_t Kt,
                                uint32_t Vt, uint32_t Dt, int32_t kb0, bool mask, bool docs, float c, int lane) {
+  static_assert(DQB == 1, "one 32-row query block per wave");
+  constexpr int NKD = D / 16, NDB = D / 32, NG = 2 * NDB;   // d steps; d blocks; dQ MFMAs per half
   const int hh = lane >> 5;
-  f32x16 s0[DQB], dp0[DQB], s1[DQB], dp1[DQB];
-  bf16x8 ds0[DQB][2], ds1[DQB][2];
-  sdp_half<D>(st, rr, Kt, Vt, 0, s0, dp0);
+  f32x16 s0, dp0, s1, dp1;
+  bf16x8 ds0[2], ds1[2];
+  bf16x8 rk[2], rv[2];   // K, V row operands (S^T, dP^T)
+  bf16x8 ga[2];          // K^T operands (dQ^T)
+  auto ds_elem = [&](const f32x16& s, const f32x16& dp, bf16x8 (&dsf)[2], int r) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, st.nl[0]));
+    dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - st.dl[0]));
+  };
+  // step j of the tile's 2*NKD S/dP steps: key half j / NKD, d step j % NKD
+  auto ld_row = [&](int j) {
+    rk[j & 1] = rr.at(Kt, j / NKD, j % NKD);
+    rv[j & 1] = rr.at(Vt, j / NKD, j % NKD);
+  };
+  // dQ MFMA g of the tile's 2*NG: key half g / NG, 16-key slot (g % NG) / NDB, d block g % NDB
+  auto ld_tr = [&](int g) { ga[g & 1] = tr.at(Kt, 32 * (g / NG) + 16 * ((g % NG) / NDB), g % NDB); };
+
+  ld_row(0);
+  ld_row(1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kd = 0; kd < NKD; ++kd) {   // half 0
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rk[kd & 1], st.qf[0][kd], kd ? s0 : f32x16{}, 0, 0, 0);
+    dp0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv[kd & 1], st.of[0][kd], kd ? dp0 : f32x16{}, 0, 0, 0);
+    ld_row(kd + 2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if (mask) dq_mask<D>(st, s0, Dt, kb0, 0, docs, hh);
-  sdp_half<D>(st, rr, Kt, Vt, 1, s1, dp1);
-  ds_half<D>(st, s0, dp0, c, ds0);
-  keep_live(ds0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kd = 0; kd < NKD; ++kd) {   // half 1 beside half 0's dS
+    const int j = NKD + kd;
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rk[j & 1], st.qf[0][kd], kd ? s1 : f32x16{}, 0, 0, 0);
+    dp1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rv[j & 1], st.of[0][kd], kd ? dp1 : f32x16{}, 0, 0, 0);
+    if (j + 2 < 2 * NKD) ld_row(j + 2);
+    else ld_tr(j + 2 - 2 * NKD);
+#pragma unroll
+    for (int e = 0; e < 16 / NKD; ++e) ds_elem(s0, dp0, ds0, kd * (16 / NKD) + e);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if (mask) dq_mask<D>(st, s1, Dt, kb0, 32, docs, hh);
-  dq_half<D>(st, tr, Kt, 0, ds0);
-  ds_half<D>(st, s1, dp1, c, ds1);
-  keep_live(ds1);
-  dq_half<D>(st, tr, Kt, 1, ds1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < 2 * NG; ++g) {   // dQ of half 0 beside half 1's dS, then half 1
+    const int t = (g % NG) / NDB, db = g % NDB;
+    st.acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[g & 1], g < NG ? ds0[t] : ds1[t], st.acc[0][db], 0,
+                                                            0, 0);
+    if (g + 2 < 2 * NG) ld_tr(g + 2);
+    if (g < NG) {
+#pragma unroll
+      for (int e = 0; e < 16 / NG; ++e) ds_elem(s1, dp1, ds1, g * (16 / NG) + e);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 template <int D>
