@@ -48,7 +48,10 @@
  *     dv [Lk, hkv, d] are contiguous.  lse and delta are [hq, Lq] fp32
  *     (natural log), row-major.
  *   - Supported: d in {64, 128}; hq % hkv == 0 with hq/hkv a power of two
- *     <= 64; 16-byte aligned pointers and strides (CP_ERR_ALIGN otherwise).
+ *     <= 64; 16-byte aligned pointers and strides (CP_ERR_ALIGN otherwise);
+ *     token strides of at most 16 MiB and spans of at most 2^29 tokens
+ *     (CP_ERR_UNSUPPORTED otherwise: the kernels address a tile of up to 128
+ *     tokens, and a per-token fp32 row, through 32-bit byte offsets).
  *   - Document ids are int32 per local token, >= 0 and non-decreasing along
  *     local order (positions increase along local order, so this is global
  *     order).  This is a precondition, not checked on the device: ids that

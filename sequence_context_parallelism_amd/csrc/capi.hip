@@ -47,6 +47,12 @@ bool valid_dtype(cp_dtype t) { return t == CP_BF16 || t == CP_F32; }
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
+// Per-row arrays (LSE, Delta, doc ids) are read through 32-bit byte offsets
+// (4 bytes per token) and token tiles through 32-bit offsets from the tile's
+// first token (128 tokens at most); both stay below 2^31.
+constexpr int32_t kMaxTokens = 1 << 29;
+constexpr int64_t kMaxStrideBytes = int64_t(1) << 24;
+
 cp_status check_shape(const cp_shape* sh) {
   if (!sh) return fail(CP_ERR_ARG, "shape is NULL");
   if (sh->hq <= 0 || sh->hkv <= 0) return fail(CP_ERR_ARG, "hq=%d and hkv=%d must be positive", sh->hq, sh->hkv);
@@ -63,12 +69,17 @@ cp_status check_shape(const cp_shape* sh) {
   if (sh->kv_stride < (int64_t)sh->hkv * sh->d) return fail(CP_ERR_ARG, "kv_stride %lld < hkv*d", (long long)sh->kv_stride);
   if ((sh->q_stride * esz) % 16 || (sh->kv_stride * esz) % 16)
     return fail(CP_ERR_ALIGN, "token strides must be multiples of 16 bytes");
+  // tiles of up to 128 tokens are copied through 32-bit byte offsets from the
+  // tile's first token, bounded by 2^31 - 1
+  if (sh->q_stride * (int64_t)esz > kMaxStrideBytes || sh->kv_stride * (int64_t)esz > kMaxStrideBytes)
+    return fail(CP_ERR_UNSUPPORTED, "token strides above %lld bytes are not supported", (long long)kMaxStrideBytes);
   return CP_OK;
 }
 
 cp_status check_span(const cp_span& s, const char* name) {
   if (s.len[0] < 0 || s.len[1] < 0) return fail(CP_ERR_ARG, "%s: negative length", name);
-  if ((int64_t)s.len[0] + s.len[1] > INT32_MAX) return fail(CP_ERR_ARG, "%s: too long", name);
+  if ((int64_t)s.len[0] + s.len[1] > kMaxTokens)
+    return fail(CP_ERR_UNSUPPORTED, "%s: more than %d tokens", name, kMaxTokens);
   if (s.len[1] > 0 && s.pos[1] < s.pos[0] + s.len[0])
     return fail(CP_ERR_ARG, "%s: second run must start at or after the end of the first", name);
   return CP_OK;
@@ -191,7 +202,7 @@ cp_status check_ring_args(const cp_shape* sh, int64_t S, int32_t P, int32_t rank
   CP_TRY(check_shape(sh));
   if (P < 1) return fail(CP_ERR_ARG, "P=%d must be >= 1", P);
   if (S <= 0 || S % (2 * (int64_t)P) != 0) return fail(CP_ERR_ARG, "S=%lld must be a positive multiple of 2P=%d", (long long)S, 2 * P);
-  if (S > INT32_MAX) return fail(CP_ERR_ARG, "S=%lld too large", (long long)S);
+  if (S > kMaxTokens) return fail(CP_ERR_UNSUPPORTED, "S=%lld above %d tokens", (long long)S, kMaxTokens);
   if (rank < -1 || rank >= P) return fail(CP_ERR_ARG, "rank=%d out of [-1, P)", rank);
   return CP_OK;
 }
@@ -597,7 +608,8 @@ cp_status cp_ulysses_share(const cp_shape* sh_full, int64_t S, int32_t sp, int32
                            const void* dout, float* dq, float* dk, float* dv, void* workspace, size_t ws_bytes,
                            void* stream) {
   CP_TRY(check_shape(sh_full));
-  if (S <= 0 || S > INT32_MAX) return fail(CP_ERR_ARG, "S=%lld out of range", (long long)S);
+  if (S <= 0) return fail(CP_ERR_ARG, "S=%lld out of range", (long long)S);
+  if (S > kMaxTokens) return fail(CP_ERR_UNSUPPORTED, "S=%lld above %d tokens", (long long)S, kMaxTokens);
   if (sp < 1 || sp_rank < 0 || sp_rank >= sp) return fail(CP_ERR_ARG, "sp=%d, sp_rank=%d", sp, sp_rank);
   if (sh_full->hq % sp || sh_full->hkv % sp)
     return fail(CP_ERR_ARG, "sp=%d must divide hq=%d and hkv=%d (KV heads bound the Ulysses degree)", sp,

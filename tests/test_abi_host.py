@@ -81,6 +81,8 @@ def _fwd_status(lib, shape, qs=None, ks=None, ptr=0x10000):
     (dict(q_stride=8 * 128 + 4), cp.CP_ERR_ALIGN),
     (dict(scale=-1.0), cp.CP_ERR_ARG),
     (dict(hkv=0), cp.CP_ERR_ARG),
+    (dict(q_stride=(1 << 23) + 8), cp.CP_ERR_UNSUPPORTED),  # > 16 MiB between tokens
+    (dict(kv_stride=(1 << 23) + 8), cp.CP_ERR_UNSUPPORTED),
 ])
 def test_validation_errors_before_launch(lib, kw, status):
     assert _fwd_status(lib, _shape(**kw)) == status
@@ -97,6 +99,9 @@ def test_span_and_pointer_errors(lib):
     one_doc.len[0] = 64
     one_doc.doc = 0x1000
     assert _fwd_status(lib, sh, qs=one_doc) == cp.CP_ERR_DOCS
+    # spans past 2^29 tokens: per-token rows are addressed with 32-bit byte offsets
+    assert _fwd_status(lib, sh, ks=cp.make_span(0, (1 << 29) + 64)) == cp.CP_ERR_UNSUPPORTED
+    assert _fwd_status(lib, sh, qs=cp.make_span(0, 1 << 28, 1 << 28, (1 << 28) + 64)) == cp.CP_ERR_UNSUPPORTED
     # empty query span: nothing to do, success without touching memory
     assert _fwd_status(lib, sh, qs=cp.make_span(0, 0)) == cp.CP_OK
 
@@ -107,6 +112,12 @@ def test_ring_and_ulysses_argument_errors(lib):
     st = lib.cp_ring_emulate(ctypes.byref(sh), 1000, 8, 0, P, P, P, None, P, cp.CP_BF16, P,
                              None, None, None, None, None, None, None, 0, None)
     assert st == cp.CP_ERR_ARG                                  # 1000 % 16 != 0
+    st = lib.cp_ring_emulate(ctypes.byref(sh), (1 << 29) + 16, 8, 0, P, P, P, None, P, cp.CP_BF16, P,
+                             None, None, None, None, None, None, None, 0, None)
+    assert st == cp.CP_ERR_UNSUPPORTED                          # above 2^29 tokens
+    st = lib.cp_ulysses_share(ctypes.byref(sh), (1 << 29) + 16, 2, 0, P, P, P, None, P, cp.CP_BF16, P,
+                              None, None, None, None, None, 0, None)
+    assert st == cp.CP_ERR_UNSUPPORTED
     st = lib.cp_ring_emulate(ctypes.byref(sh), 1024, 8, 0, P, P, P, None, P, cp.CP_BF16, P,
                              None, None, None, None, None, None, None, 0, None)
     assert st == cp.CP_ERR_WORKSPACE
