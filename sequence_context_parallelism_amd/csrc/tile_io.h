@@ -51,23 +51,35 @@ struct Swz {
   }
 };
 
-// Direct-to-LDS loads are issued as buffer loads (buffer_load ... lds)
-// through a raw buffer resource on a wave-uniform base, with a per-lane byte
-// offset, rather than as global_load_lds: while a global_load_lds is in
-// flight the compiler treats LDS completions as unordered and waits for
-// every outstanding LDS read at each use, which defeats register
-// prefetching of MFMA operands; with buffer loads it keeps exact counts.
+// Direct-to-LDS loads are buffer loads (buffer_load ... lds) through a raw
+// buffer resource on a wave-uniform base, with a per-lane byte offset.  They
+// are written as inline asm, so the compiler does not track them: it treats
+// a tracked LDS DMA as a possible writer of any LDS that an LDS transpose read
+// (ds_read_b64_tr_b16) touches, and waits for every load in flight
+// (s_waitcnt vmcnt(0)) before the first such read after it, which stalls a
+// wave mid-tile on the next tile's copy.  Every kernel here reads a copied
+// tile only after its own s_waitcnt vmcnt(0) and a work-group barrier, which
+// is what makes the copy visible; the asm has no output register (the data
+// goes to LDS at M0 + 16 lane), and loads complete in issue order, so the
+// compiler's own vmcnt waits for its tracked loads stay correct (an untracked
+// load in flight only makes them wait longer).  The compiler's hazard checks
+// do not look inside inline asm, so the asm brings its own wait states: the
+// s_nop 4 covers the 5 that a VMEM instruction needs after a VALU write of an
+// SGPR it reads (the resource descriptor may have just been reloaded from a
+// spill lane with v_readlane) and the 1 that an LDS DMA needs after M0 is
+// written.
 __device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
 }
 // 16 bytes per lane at base + voff into LDS [lds + 16 lane, +16)
 __device__ inline void buf_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, CP_LDS_AT(lds), 16, voff, 0, 0, 0);
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds) : "memory");
 }
 // One 4-byte element per lane: element `idx` of the array at `base` into LDS
 // [lds + 4 lane, +4).
 __device__ inline void row_load_lds(const void* base, int32_t idx, uint32_t lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(base), CP_LDS_AT(lds), 4, (uint32_t)idx * 4u, 0, 0, 0);
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"((uint32_t)idx * 4u), "s"(buf_rsrc(base)),
+               "{m0}"(lds) : "memory");
 }
 
 // Issue the direct-to-LDS loads of an R x D tile at LDS address `dst` whose
