@@ -25,6 +25,8 @@ CASES = [
     ("tiny_5x7", 4, 2, 128, (2, 5), (0, 7), True, False),               # one partial tile each way
     ("mqa_g16", 16, 1, 128, (0, 150), (0, 150), True, False),           # 16 query heads on one KV head
     ("one_row_half_one_key_block", 4, 1, 128, (0, 33), (0, 129), False, False),   # 2nd query half: 1 row
+    ("all_rows_empty", 4, 2, 128, (0, 40), (100, 64), True, False),   # every key after every query
+    ("no_keys", 4, 2, 64, (0, 70), (0, 0), True, False),              # empty key span
 ]
 
 
