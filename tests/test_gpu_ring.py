@@ -55,11 +55,12 @@ def test_tiny_ring_fp32_every_step(gpu_lib):
         assert lse_err(host(lse), full_l[:, rows]) <= 1e-6
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("docs", [False, True], ids=["causal", "docs"])
-def test_ring_forward_backward_one_rank(gpu_lib, dtype, docs):
-    S, P, hq, hkv, d = 768, 3, 8, 2, 128
-    print(f"ring one rank {dtype} docs={docs}", flush=True)
+def test_ring_forward_backward_one_rank(gpu_lib, dtype, docs, d):
+    S, P, hq, hkv = 768, 3, 8, 2
+    print(f"ring one rank {dtype} docs={docs} d={d}", flush=True)
     (qh, kh, vh, doh), (qd, kd, vd, dod), doc = _ring_inputs(S, P, hq, hkv, d, dtype, 7, docs)
     doc_d = None if doc is None else torch.from_numpy(doc).to(DEV)
     sh = shape_for(hq, hkv, d, dtype)
@@ -114,9 +115,10 @@ def test_ring_all_ranks_full_gradient(gpu_lib):
     assert max_abs(host(dv), rdv[order]) <= grad_tol(rdv, tol["grad"])
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-def test_ulysses_share_is_head_slice(gpu_lib, dtype):
-    S, hq, hkv, d, sp = 640, 16, 4, 128, 2
+def test_ulysses_share_is_head_slice(gpu_lib, dtype, d):
+    S, hq, hkv, sp = 640, 16, 4, 2
     (qh, kh, vh, _), (qd, kd, vd, _), _ = _ring_inputs(S, 1, hq, hkv, d, dtype, 21)
     sh = shape_for(hq, hkv, d, dtype)
     tol = TOL[dtype]
