@@ -462,6 +462,13 @@ def main():
                 e["gb_s"] = round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1)
                 e["frac_hbm_8tbs"] = round(r["bytes"] / (r["ms"] * 1e-3) / 8e12, 3)
             out["kernels"][name] = e
+        # forward-only and backward-only causal-FLOP throughput of the launches
+        # timed alone (the backward's Delta pass, ~0.2 % of it, is not included)
+        if all(n in kt for n in ("fwd_bf16_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel")):
+            bwd_ms = kt["dkdv_bf16_kernel"]["ms"] + kt["dq_bf16_kernel"]["ms"]
+            bwd_flops = kt["dkdv_bf16_kernel"]["flops"] + kt["dq_bf16_kernel"]["flops"]
+            out["forward_tflops"] = round(kt["fwd_bf16_kernel"]["flops"] / (kt["fwd_bf16_kernel"]["ms"] * 1e-3) / 1e12, 1)
+            out["backward_tflops"] = round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1)
         dom = max((n for n in kt if "flops" in kt[n]), key=lambda n: kt[n]["ms"])
         ach = kt[dom]["flops"] / (kt[dom]["ms"] * 1e-3) / 1e12
         traffic = measured_traffic(dom, args.workload)
