@@ -437,18 +437,20 @@ cp_status ring_drive(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, con
   }
 
   // emulated traffic: events [0] start, [1] forward end, [2] end; then per
-  // pass (forward, backward) P "shard received" and P "step computed" events
+  // pass (forward, backward) P "shard received" and P "step computed" events;
+  // then P "step's dK/dV computed" events of the backward
   EventSet ev;
   cp_shape shc = *sh;                                     // receive rows are compact
   shc.kv_stride = kvrow;
   const size_t shard_b = (size_t)n * kvrow * in_esz;     // K (or V) rows of one shard
   if (ov) {
-    CP_TRY_HIP(ev.make(3 + 4 * (size_t)P), "ring events");
+    CP_TRY_HIP(ev.make(3 + 5 * (size_t)P), "ring events");
     CP_TRY_HIP(hipEventRecord(ev.e[0], st), "ring event");
     CP_TRY_HIP(hipStreamWaitEvent(ov->cs, ev.e[0], 0), "ring wait");   // earlier readers of the areas
   }
   auto ev_ready = [&](int pass, int32_t s) { return ev.e[3 + (size_t)pass * 2 * P + s]; };
   auto ev_done = [&](int pass, int32_t s) { return ev.e[3 + (size_t)pass * 2 * P + P + s]; };
+  auto ev_dkdv = [&](int32_t s) { return ev.e[3 + 4 * (size_t)P + s]; };
   // Before step s computes: the shard of step s + 1 into recv[(s + 1) & 1],
   // once step s - 1 (its last reader) is done.
   auto prefetch = [&](int pass, int32_t r, int32_t s) -> hipError_t {
@@ -537,13 +539,21 @@ cp_status ring_drive(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, con
         const cp_span ks = run_span((int64_t)j * c, c, (int64_t)(2 * P - 1 - j) * c, c, doc ? doc + j * n : nullptr);
         float* dkj = dk + (size_t)j * n * kvrow;
         float* dvj = dv + (size_t)j * n * kvrow;
-        CP_TRY_HIP(run_bwd(shs, qr, qs, kj, vj, ks, dout_r, lse_r, dlt, n, dq_r, dkj, dvj, st), "ring backward step");
-        if (ov) {   // the step's dK/dV shard leaves for its owner
+        if (!ov) {
+          CP_TRY_HIP(run_bwd(shs, qr, qs, kj, vj, ks, dout_r, lse_r, dlt, n, dq_r, dkj, dvj, st),
+                     "ring backward step");
+        } else {   // dK/dV first: the step's dK/dV shard leaves for its owner while dQ runs
           const size_t gb = (size_t)n * kvrow * 4;
-          CP_TRY_HIP(hipEventRecord(ev_done(1, s), st), "ring event");
-          CP_TRY_HIP(hipStreamWaitEvent(ov->cs, ev_done(1, s), 0), "ring wait");
+          CP_TRY_HIP(run_bwd(shs, qr, qs, kj, vj, ks, dout_r, lse_r, dlt, n, dq_r, dkj, dvj, st, BWD_DKDV),
+                     "ring backward step (dK/dV)");
+          CP_TRY_HIP(hipEventRecord(ev_dkdv(s), st), "ring event");
+          CP_TRY_HIP(hipStreamWaitEvent(ov->cs, ev_dkdv(s), 0), "ring wait");
           CP_TRY_HIP(hipMemcpyAsync(ov->send, dkj, gb, hipMemcpyDeviceToDevice, ov->cs), "ring send copy");
           CP_TRY_HIP(hipMemcpyAsync((char*)ov->send + gb, dvj, gb, hipMemcpyDeviceToDevice, ov->cs), "ring send copy");
+          CP_TRY_HIP(run_bwd(shs, qr, qs, kj, vj, ks, dout_r, lse_r, dlt, n, dq_r, dkj, dvj, st, BWD_DQ),
+                     "ring backward step (dQ)");
+          // the step's last reader of its receive area
+          CP_TRY_HIP(hipEventRecord(ev_done(1, s), st), "ring event");
         }
       }
     }

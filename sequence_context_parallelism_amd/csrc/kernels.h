@@ -57,7 +57,7 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);       // dkdv then dq
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);       // dq then dkdv
 hipError_t launch_bwd_bf16_dkdv(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16_dq(const BwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
