@@ -3,8 +3,8 @@
 Default workload: the Ulysses share of a Llama-3.1-8B-shaped layer at SP=4:
 the full S=65536 causal sequence for this GPU's 8 query heads / 2 KV heads,
 d=128, bf16, forward + backward (dO ~ N(0,1)).  One step = one
-cp_ulysses_share call with the backward (zero-fill of the gradients, forward
-chunk attention, Delta, backward chunk attention), all in libcpattn's kernels.
+cp_ulysses_share call with the backward (forward chunk attention, Delta,
+backward chunk attention writing the gradients), all in libcpattn's kernels.
 
 Prints ONE JSON line.  ``value`` is the causal-FLOP throughput of the step:
 algorithmic FLOPs (4*d per allowed (query, key) pair per query head forward,
