@@ -165,7 +165,7 @@ def kernel_times(wl, cp, torch, iters):
     o32 = torch.empty(wl.rows, wl.hq, wl.d, device=wl.dev)
     lse2 = torch.empty_like(wl.lse)
     o_part = torch.empty_like(o32)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     cp.cp_attn_chunk_fwd(wl.sh, wl.q, qs, k, v, ks, wl.o, wl.lse)
     cp.cp_attn_delta(wl.o, wl.dout, wl.delta)
     cp.cp_attn_chunk_fwd(wl.sh, wl.q, qs, k, v, ks, o_part, lse2)
@@ -183,8 +183,11 @@ def kernel_times(wl, cp, torch, iters):
     for _ in range(iters):      # merge a partial into an accumulator of the output's shape
         cp.cp_lse_merge(o32, lse2, o_part, wl.lse)
     ev[4].record(st)
+    for _ in range(iters):      # the backward's Delta = rowsum(dO * O) of the final output
+        cp.cp_attn_delta(wl.o, wl.dout, wl.delta)
+    ev[5].record(st)
     torch.cuda.synchronize()
-    ms = [ev[i].elapsed_time(ev[i + 1]) / iters for i in range(4)]
+    ms = [ev[i].elapsed_time(ev[i + 1]) / iters for i in range(5)]
     rh = wl.rows * wl.hq
     extra = {}
     if wl.name == "ulysses_64k":
@@ -220,6 +223,7 @@ def kernel_times(wl, cp, torch, iters):
         "dkdv_bf16_kernel": {"ms": ms[1], "flops": 4 * unit, "flops_executed": 4 * unit},
         "dq_bf16_kernel": {"ms": ms[2], "flops": 1 * unit, "flops_executed": 3 * unit},
         "merge_kernel": {"ms": ms[3], "bytes": rh * (3 * wl.d * 4 + 3 * 4)},
+        "delta_kernel": {"ms": ms[4], "bytes": rh * (2 * wl.d * 2 + 4)},   # read O, dO (bf16), write Delta
         **extra,
     }
 

@@ -94,6 +94,30 @@ __global__ __launch_bounds__(256) void delta_kernel(int64_t rows, int h, const T
   if (in && piece == 0) delta[(int64_t)(rh % h) * ld + rh / h] = acc;
 }
 
+// The same for bf16 O and dO with 16-byte loads: SEG = d / 8 lanes per
+// (row, head), 8 elements each.
+template <int SEG>
+__global__ __launch_bounds__(256) void delta_bf16_kernel(int64_t rows, int h, const __bf16* __restrict__ o,
+                                                         const __bf16* __restrict__ dout, float* __restrict__ delta,
+                                                         int64_t ld) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rh = gt / SEG;
+  const int piece = (int)(gt % SEG);
+  const bool in = rh < rows * h;
+  float acc = 0.f;
+  if (in) {
+    const int64_t base = rh * (SEG * 8) + piece * 8;
+    const bf16x8 a = *(const bf16x8*)(o + base);
+    const bf16x8 b = *(const bf16x8*)(dout + base);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += (float)a[i] * (float)b[i];
+  }
+#pragma unroll
+  for (int off = SEG / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (in && piece == 0) delta[(int64_t)(rh % h) * ld + rh / h] = acc;
+}
+
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(int64_t n, const float* __restrict__ src,
                                                           __bf16* __restrict__ dst) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -166,7 +190,8 @@ static hipError_t delta_dispatch(int64_t rows, int h, const void* o, int o_f32, 
   else if (dout_f32)
     hipLaunchKernelGGL((delta_kernel<SEG, __bf16, float>), dim3(grid), dim3(256), 0, stream, rows, h, (const __bf16*)o, (const float*)dout, delta, ld);
   else
-    hipLaunchKernelGGL((delta_kernel<SEG, __bf16, __bf16>), dim3(grid), dim3(256), 0, stream, rows, h, (const __bf16*)o, (const __bf16*)dout, delta, ld);
+    hipLaunchKernelGGL((delta_bf16_kernel<SEG / 2>), dim3(blocks_for(rows * h * (SEG / 2))), dim3(256), 0, stream, rows, h,
+                       (const __bf16*)o, (const __bf16*)dout, delta, ld);
   return hipGetLastError();
 }
 
