@@ -54,3 +54,13 @@ def test_traffic_summary_is_complete_and_consistent(name):
 
 def test_reader_returns_none_without_a_summary():
     assert bench.measured_traffic("fwd_bf16_kernel", "no_such_workload") is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The library is one GPU's share: bench.py --gpus N>1 exits with a message
+    (before touching a GPU)."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--gpus 2 is not supported" in r.stderr
