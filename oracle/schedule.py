@@ -41,15 +41,33 @@ def zigzag_layout(S, P, r):
     return (r * c, (2 * P - 1 - r) * c), (c, c)
 
 
-def rank_positions(S, P, r):
-    """Global positions of rank r's local tokens, in local order."""
-    (p0, p1), (l0, l1) = zigzag_layout(S, P, r)
+def pair_layout(S, P, r, chunks):
+    """Rank r's two chunks under an explicit two-chunks-per-rank assignment:
+    chunks[r] = (a, b) with a < b, every chunk 0..2P-1 used once.  Same
+    return form as zigzag_layout."""
+    if P < 1 or S < 1 or S % (2 * P) != 0 or not 0 <= r < P:
+        raise ValueError("need P >= 1, S > 0 divisible by 2P and 0 <= r < P")
+    flat = sorted(int(x) for pair in chunks for x in pair)
+    if len(chunks) != P or flat != list(range(2 * P)):
+        raise ValueError("chunks must give each of the P ranks two of the 2P chunks, each chunk once")
+    a, b = (int(x) for x in chunks[r])
+    if not a < b:
+        raise ValueError("a rank's chunks must be in increasing order")
+    c = S // (2 * P)
+    return (a * c, b * c), (c, c)
+
+
+def rank_positions(S, P, r, chunks=None):
+    """Global positions of rank r's local tokens, in local order (zigzag, or
+    the assignment ``chunks`` of pair_layout)."""
+    lay = zigzag_layout(S, P, r) if chunks is None else pair_layout(S, P, r, chunks)
+    (p0, p1), (l0, l1) = lay
     return np.concatenate([np.arange(p0, p0 + l0), np.arange(p1, p1 + l1)])
 
 
-def sharded_order(S, P):
+def sharded_order(S, P, chunks=None):
     """Global position of each row of a sharded-order array."""
-    return np.concatenate([rank_positions(S, P, r) for r in range(P)])
+    return np.concatenate([rank_positions(S, P, r, chunks) for r in range(P)])
 
 
 def ring_source(P, r, s):
@@ -91,22 +109,23 @@ def _shard(x, S, P, r):
     return x[r * c2:(r + 1) * c2]
 
 
-def ring_forward(q, k, v, S, P, r, *, scale, causal=True, doc=None):
-    """Rank r's forward under the ring, all inputs in sharded order.
+def ring_forward(q, k, v, S, P, r, *, scale, causal=True, doc=None, chunks=None):
+    """Rank r's forward under the ring, all inputs in sharded order (of the
+    zigzag layout, or of the assignment ``chunks``, see pair_layout).
 
     At each step the rank's Q shard attends to the visiting KV shard (every
     mask entry evaluated on global positions), and the partial (O, LSE) is
     merged into the running result.  Returns (o, lse, steps) where steps is the
     list of per-step partials (o_s, lse_s).
     """
-    qpos = rank_positions(S, P, r)
+    qpos = rank_positions(S, P, r, chunks)
     qd = None if doc is None else _shard(doc, S, P, r)
     qs = _shard(q, S, P, r)
     o = lse = None
     steps = []
     for s in range(P):
         j = ring_source(P, r, s)
-        kpos = rank_positions(S, P, j)
+        kpos = rank_positions(S, P, j, chunks)
         kd = None if doc is None else _shard(doc, S, P, j)
         po, pl = A.forward(qs, _shard(k, S, P, j), _shard(v, S, P, j), qpos, kpos,
                            scale=scale, causal=causal, qdoc=qd, kdoc=kd)
@@ -118,15 +137,16 @@ def ring_forward(q, k, v, S, P, r, *, scale, causal=True, doc=None):
     return o, lse, steps
 
 
-def ring_backward(q, k, v, dout, o, lse, S, P, r, *, scale, causal=True, doc=None):
-    """Rank r's backward under the ring (sharded order).
+def ring_backward(q, k, v, dout, o, lse, S, P, r, *, scale, causal=True, doc=None, chunks=None):
+    """Rank r's backward under the ring (sharded order; ``chunks`` as in
+    ring_forward).
 
     Delta comes from the rank's final O; each step's chunk backward uses the
     final LSE.  Returns (dq of the rank's rows, dk, dv over all S rows) where
     dk/dv hold only this rank's query rows' contributions, each in the
     visiting rank's slot: what a ring carries back to each KV owner.
     """
-    qpos = rank_positions(S, P, r)
+    qpos = rank_positions(S, P, r, chunks)
     qd = None if doc is None else _shard(doc, S, P, r)
     qs = _shard(q, S, P, r)
     dlt = A.delta(o, dout)
@@ -138,7 +158,7 @@ def ring_backward(q, k, v, dout, o, lse, S, P, r, *, scale, causal=True, doc=Non
         j = ring_source(P, r, s)
         kd = None if doc is None else _shard(doc, S, P, j)
         gq, gk, gv = A.backward(qs, _shard(k, S, P, j), _shard(v, S, P, j), dout,
-                                lse, dlt, qpos, rank_positions(S, P, j),
+                                lse, dlt, qpos, rank_positions(S, P, j, chunks),
                                 scale=scale, causal=causal, qdoc=qd, kdoc=kd)
         dq += gq
         dk[j * c2:(j + 1) * c2] += gk
