@@ -53,9 +53,14 @@
  *     (CP_ERR_UNSUPPORTED otherwise: the kernels address a tile of up to 128
  *     tokens, and a per-token fp32 row, through 32-bit byte offsets).
  *   - Document ids are int32 per local token, >= 0 and non-decreasing along
- *     local order (positions increase along local order, so this is global
- *     order).  This is a precondition, not checked on the device: ids that
- *     break it give wrong (but finite, in-bounds) results.
+ *     global order (positions increase along a span's local order, so a
+ *     span's ids are non-decreasing too).  The kernels rely on this: with ids
+ *     that break it, tiles are classified from wrong id ranges and results
+ *     are wrong (possibly not finite); memory accesses stay in bounds.  Set
+ *     CP_CHECK_DOCS in cp_shape.flags to have every call that takes ids check
+ *     them first (a host copy, so the call waits for its stream) and return
+ *     CP_ERR_DOCS, with nothing enqueued, when an id is negative or
+ *     decreases; cp_check_docs checks an array on its own.
  *   - Not thread-safe per stream: calls on one stream are ordered by the
  *     stream; calls that write the same outputs from different streams race.
  */
@@ -69,14 +74,14 @@
 extern "C" {
 #endif
 
-#define CP_ABI_VERSION 1
+#define CP_ABI_VERSION 2
 
 typedef enum {
   CP_OK = 0,
   CP_ERR_ARG = -1,          /* invalid argument (null pointer, bad size or count) */
   CP_ERR_UNSUPPORTED = -2,  /* valid but not implemented (d, head ratio)          */
   CP_ERR_ALIGN = -3,        /* pointer or stride not 16-byte aligned             */
-  CP_ERR_DOCS = -4,         /* doc ids given for only one side                   */
+  CP_ERR_DOCS = -4,         /* doc ids for only one side, or (checked) ids < 0 or decreasing */
   CP_ERR_WORKSPACE = -5,    /* workspace missing or too small                     */
   CP_ERR_HIP = -6           /* a HIP launch failed                                */
 } cp_status;
@@ -103,7 +108,15 @@ typedef struct {
   float scale;          /* softmax scale on q.k (1/sqrt(d) in the usual reading)   */
   int32_t causal;       /* 1: mask keys after the query (diagonal included)       */
   cp_dtype dtype;       /* element type of q, k, v and dout                        */
+  int32_t flags;        /* 0 or CP_CHECK_DOCS; other bits are CP_ERR_ARG           */
 } cp_shape;
+
+/* cp_shape.flags: check document ids before anything is enqueued
+ * ([Llama3] "네 병렬화는 서로 다른 자원을 확보하는 방식": the document mask must
+ * survive context parallelism, so ids that cannot describe packed documents
+ * are refused rather than silently misread).  Costs a device-to-host copy of
+ * the ids and a wait for the stream. */
+#define CP_CHECK_DOCS 1
 
 /* Forward attention of a Q chunk against one KV chunk: the partial result a
  * ring step produces before merging ([MaxText] "헤드를 나누거나, KV를 돌리거나").
@@ -201,6 +214,22 @@ cp_status cp_ring_emulate(const cp_shape *sh, int64_t S, int32_t P, int32_t rank
                           float *step_o, float *step_lse,
                           void *workspace, size_t ws_bytes, void *stream);
 
+/* cp_ring_emulate under an explicit two-chunks-per-rank layout instead of
+ * zigzag ([Llama3] "긴 문맥은 어텐션 비용 이상을 바꾸는 방식": with packed
+ * documents the ranks are balanced by attention work, e.g. by the pairing
+ * cp_balanced_pairs returns).  chunks: HOST array of 2P int32, rank r holds
+ * the S/(2P)-token chunks chunks[2r] < chunks[2r+1], each chunk exactly once
+ * (CP_ERR_ARG otherwise); the zigzag table is chunks = {r, 2P-1-r}.  Inputs
+ * are in the sharded order of this layout (rank 0's two chunks, then rank
+ * 1's, ...); step s still brings rank (r - s) mod P's shard.  Outputs,
+ * workspace (cp_ring_workspace_bytes) and everything else as for
+ * cp_ring_emulate, without per-step capture. */
+cp_status cp_ring_emulate_layout(const cp_shape *sh, int64_t S, int32_t P, int32_t rank, const int32_t *chunks,
+                                 const void *q, const void *k, const void *v, const int32_t *doc,
+                                 void *o, cp_dtype o_dtype, float *lse,
+                                 const void *dout, float *dq, float *dk, float *dv,
+                                 void *workspace, size_t ws_bytes, void *stream);
+
 /* Workspace bytes cp_ring_emulate_overlap needs (0 on bad args). */
 size_t cp_ring_overlap_workspace_bytes(const cp_shape *sh, int64_t S, int32_t P,
                                        cp_dtype o_dtype, int32_t backward);
@@ -265,6 +294,14 @@ cp_status cp_allgather_share(const cp_shape *sh, int64_t S, int32_t P, int32_t r
                              void *o, cp_dtype o_dtype, float *lse,
                              const void *dout, float *dq, float *dk, float *dv,
                              void *workspace, size_t ws_bytes, void *stream);
+
+/* Checks n document ids: each >= 0 and none smaller than the one before
+ * ([Llama3] "네 병렬화는 서로 다른 자원을 확보하는 방식": packed documents keep
+ * their mask).  doc: a HOST array if on_host != 0, else a device array that
+ * is copied to the host on `stream` (the call then waits for the stream).
+ * CP_OK, or CP_ERR_DOCS naming the first offending index; CP_ERR_ARG for
+ * n < 0 or a NULL doc with n > 0. */
+cp_status cp_check_docs(const int32_t *doc, int64_t n, int32_t on_host, void *stream);
 
 /* Causal work of the 2P chunks of a sequence ([Llama3] "긴 문맥은 어텐션
  * 비용 이상을 바꾸는 방식": balance ranks by attention compute, not tokens):

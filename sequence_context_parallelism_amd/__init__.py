@@ -19,14 +19,16 @@ LIB_PATH = os.path.join(HERE, "libcpattn.so")
 CP_OK, CP_ERR_ARG, CP_ERR_UNSUPPORTED, CP_ERR_ALIGN, CP_ERR_DOCS, CP_ERR_WORKSPACE, CP_ERR_HIP = \
     0, -1, -2, -3, -4, -5, -6
 CP_BF16, CP_F32 = 0, 1
+CP_CHECK_DOCS = 1
 
 EXPORTED = (
     "cp_attn_chunk_fwd", "cp_lse_merge", "cp_attn_delta", "cp_attn_chunk_bwd",
     "cp_attn_chunk_bwd_dkdv", "cp_attn_chunk_bwd_dq",
     "cp_zigzag_layout", "cp_ring_schedule", "cp_ring_workspace_bytes", "cp_ring_emulate",
+    "cp_ring_emulate_layout",
     "cp_ring_overlap_workspace_bytes", "cp_ring_emulate_overlap",
     "cp_ulysses_workspace_bytes", "cp_ulysses_share", "cp_allgather_workspace_bytes", "cp_allgather_share",
-    "cp_chunk_work", "cp_balanced_pairs",
+    "cp_check_docs", "cp_chunk_work", "cp_balanced_pairs",
     "cp_a2a_tokens_to_heads", "cp_a2a_heads_to_tokens",
     "cp_tile_map", "cp_last_error", "cp_abi_version",
 )
@@ -46,7 +48,8 @@ class cp_span(ctypes.Structure):
 class cp_shape(ctypes.Structure):
     _fields_ = [("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("q_stride", ctypes.c_int64), ("kv_stride", ctypes.c_int64),
-                ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
 
 
 _lib = None
@@ -79,11 +82,14 @@ def load(path: str = LIB_PATH):
                                           P, SZ, P, P]),
         "cp_ring_emulate": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, P, P,
                                   P, SZ, P]),
+        "cp_ring_emulate_layout": (I32, [SH, I64, I32, I32, P, P, P, P, P, P, I32, P, P, P, P, P,
+                                         P, SZ, P]),
         "cp_ulysses_workspace_bytes": (SZ, [SH, I64, I32, I32]),
         "cp_ulysses_share": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, P,
                                    SZ, P]),
         "cp_allgather_workspace_bytes": (SZ, [SH, I64, I32, I32, I32]),
         "cp_allgather_share": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, P, SZ, P]),
+        "cp_check_docs": (I32, [P, I64, I32, P]),
         "cp_chunk_work": (I32, [I64, I32, P, P]),
         "cp_balanced_pairs": (I32, [I64, I32, P, P, P]),
         "cp_a2a_tokens_to_heads": (I32, [I64, I32, I32, I32, I32, I32, P, I64, P, P]),
@@ -107,6 +113,37 @@ def _check(status):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _arg_error(msg):
+    raise CpError(CP_ERR_ARG, msg)
+
+
+def _dense(name, t, shape=None):
+    """An output (or dout/lse/delta) tensor must be contiguous, on the GPU,
+    and, when ``shape`` is given, of exactly that shape: the library reads it
+    with the documented dense layout and cannot see strides."""
+    if t is None:
+        return
+    if not t.is_cuda:
+        _arg_error(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        _arg_error(f"{name} must be contiguous (shape {tuple(t.shape)}, strides {tuple(t.stride())})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        _arg_error(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _tokens(name, t, stride):
+    """q, k, v: token-major with ``stride`` elements between tokens (a head
+    slice of a wider tensor is fine) and each head row contiguous."""
+    if t is None:
+        return
+    if not t.is_cuda:
+        _arg_error(f"{name} must be a GPU tensor")
+    if t.dim() >= 2 and t.shape[0] > 1 and t.stride(0) != stride:
+        _arg_error(f"{name} token stride {t.stride(0)} differs from the shape's {stride}")
+    if t.stride(-1) != 1 or (t.dim() == 3 and t.shape[1] > 1 and t.stride(1) != t.shape[2]):
+        _arg_error(f"{name} must have contiguous head rows (strides {tuple(t.stride())})")
 
 
 def _stream(stream):
@@ -135,12 +172,17 @@ def make_span(pos0, len0, pos1=0, len1=0, doc=None):
     return s
 
 
-def make_shape(hq, hkv, d, q_stride, kv_stride, scale, causal, dtype):
+def make_shape(hq, hkv, d, q_stride, kv_stride, scale, causal, dtype, flags=0):
     sh = cp_shape()
     sh.hq, sh.hkv, sh.d = hq, hkv, d
     sh.q_stride, sh.kv_stride = q_stride, kv_stride
     sh.scale, sh.causal, sh.dtype = scale, int(bool(causal)), dtype
+    sh.flags = int(flags)
     return sh
+
+
+def _span_len(s):
+    return int(s.len[0]) + int(s.len[1])
 
 
 def cp_abi_version():
@@ -149,6 +191,11 @@ def cp_abi_version():
 
 def cp_attn_chunk_fwd(shape, q, qs, k, v, ks, o, lse, stream=None):
     lib = load()
+    _tokens("q", q, shape.q_stride)
+    _tokens("k", k, shape.kv_stride)
+    _tokens("v", v, shape.kv_stride)
+    _dense("o", o, (_span_len(qs), shape.hq, shape.d))
+    _dense("lse", lse, (shape.hq, _span_len(qs)))
     _check(lib.cp_attn_chunk_fwd(ctypes.byref(shape), _ptr(q), qs, _ptr(k), _ptr(v), ks,
                                  _ptr(o), _dtype_code(o), _ptr(lse), _stream(stream)))
 
@@ -157,6 +204,9 @@ def cp_lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
     """o_* [rows, h, d] fp32, lse_* [h, rows] fp32; acc updated in place."""
     lib = load()
     rows, h, d = o_acc.shape
+    for name, t, shp in (("o_acc", o_acc, (rows, h, d)), ("o_part", o_part, (rows, h, d)),
+                         ("lse_acc", lse_acc, (h, rows)), ("lse_part", lse_part, (h, rows))):
+        _dense(name, t, shp)
     _check(lib.cp_lse_merge(rows, h, d, _ptr(o_acc), _ptr(lse_acc), _ptr(o_part),
                             _ptr(lse_part), _stream(stream)))
 
@@ -164,12 +214,25 @@ def cp_lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
 def cp_attn_delta(o, dout, delta, stream=None):
     lib = load()
     rows, h, d = o.shape
+    _dense("o", o, (rows, h, d))
+    _dense("dout", dout, (rows, h, d))
+    _dense("delta", delta, (h, rows))
     _check(lib.cp_attn_delta(rows, h, d, _ptr(o), _dtype_code(o), _ptr(dout), _dtype_code(dout),
                              _ptr(delta), _stream(stream)))
 
 
 def cp_attn_chunk_bwd(shape, q, qs, k, v, ks, dout, lse, delta, dq, dk, dv, stream=None):
     lib = load()
+    _tokens("q", q, shape.q_stride)
+    _tokens("k", k, shape.kv_stride)
+    _tokens("v", v, shape.kv_stride)
+    lq, lk = _span_len(qs), _span_len(ks)
+    _dense("dout", dout, (lq, shape.hq, shape.d))
+    _dense("lse", lse, (shape.hq, lq))
+    _dense("delta", delta, (shape.hq, lq))
+    _dense("dq", dq, (lq, shape.hq, shape.d))
+    _dense("dk", dk, (lk, shape.hkv, shape.d))
+    _dense("dv", dv, (lk, shape.hkv, shape.d))
     _check(lib.cp_attn_chunk_bwd(ctypes.byref(shape), _ptr(q), qs, _ptr(k), _ptr(v), ks,
                                  _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk),
                                  _ptr(dv), _stream(stream)))
@@ -177,6 +240,15 @@ def cp_attn_chunk_bwd(shape, q, qs, k, v, ks, dout, lse, delta, dq, dk, dv, stre
 
 def cp_attn_chunk_bwd_dkdv(shape, q, qs, k, v, ks, dout, lse, delta, dk, dv, stream=None):
     lib = load()
+    _tokens("q", q, shape.q_stride)
+    _tokens("k", k, shape.kv_stride)
+    _tokens("v", v, shape.kv_stride)
+    lq, lk = _span_len(qs), _span_len(ks)
+    _dense("dout", dout, (lq, shape.hq, shape.d))
+    _dense("lse", lse, (shape.hq, lq))
+    _dense("delta", delta, (shape.hq, lq))
+    _dense("dk", dk, (lk, shape.hkv, shape.d))
+    _dense("dv", dv, (lk, shape.hkv, shape.d))
     _check(lib.cp_attn_chunk_bwd_dkdv(ctypes.byref(shape), _ptr(q), qs, _ptr(k), _ptr(v), ks,
                                       _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
                                       _stream(stream)))
@@ -184,6 +256,14 @@ def cp_attn_chunk_bwd_dkdv(shape, q, qs, k, v, ks, dout, lse, delta, dk, dv, str
 
 def cp_attn_chunk_bwd_dq(shape, q, qs, k, v, ks, dout, lse, delta, dq, stream=None):
     lib = load()
+    _tokens("q", q, shape.q_stride)
+    _tokens("k", k, shape.kv_stride)
+    _tokens("v", v, shape.kv_stride)
+    lq, lk = _span_len(qs), _span_len(ks)
+    _dense("dout", dout, (lq, shape.hq, shape.d))
+    _dense("lse", lse, (shape.hq, lq))
+    _dense("delta", delta, (shape.hq, lq))
+    _dense("dq", dq, (lq, shape.hq, shape.d))
     _check(lib.cp_attn_chunk_bwd_dq(ctypes.byref(shape), _ptr(q), qs, _ptr(k), _ptr(v), ks,
                                     _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _stream(stream)))
 
@@ -204,6 +284,21 @@ def cp_ring_schedule(S, P, rank, step):
     return src.value, [kind[i] for i in range(4)]
 
 
+def _ring_checks(shape, S, P, rank, q, k, v, o, lse, dout, dq, dk, dv):
+    rows = S if rank < 0 else S // P
+    _tokens("q", q, shape.q_stride)
+    _tokens("k", k, shape.kv_stride)
+    _tokens("v", v, shape.kv_stride)
+    _dense("o", o, (rows, shape.hq, shape.d))
+    _dense("lse", lse)
+    if lse is not None and lse.numel() != shape.hq * rows:
+        _arg_error(f"lse has {lse.numel()} elements, expected {shape.hq * rows}")
+    _dense("dout", dout, (rows, shape.hq, shape.d))
+    _dense("dq", dq, (rows, shape.hq, shape.d))
+    _dense("dk", dk, (S, shape.hkv, shape.d))
+    _dense("dv", dv, (S, shape.hkv, shape.d))
+
+
 def cp_ring_workspace_bytes(shape, S, P, rank, o_dtype, backward):
     return load().cp_ring_workspace_bytes(ctypes.byref(shape), S, P, rank, o_dtype, int(bool(backward)))
 
@@ -211,11 +306,32 @@ def cp_ring_workspace_bytes(shape, S, P, rank, o_dtype, backward):
 def cp_ring_emulate(shape, S, P, rank, q, k, v, doc, o, lse, dout=None, dq=None, dk=None, dv=None,
                     step_o=None, step_lse=None, workspace=None, stream=None):
     lib = load()
+    _ring_checks(shape, S, P, rank, q, k, v, o, lse, dout, dq, dk, dv)
+    _dense("step_o", step_o, (P, S // P, shape.hq, shape.d))
+    _dense("step_lse", step_lse, (P, shape.hq, S // P))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.cp_ring_emulate(ctypes.byref(shape), S, P, rank, _ptr(q), _ptr(k), _ptr(v), _ptr(doc),
                                _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                                _ptr(dv), _ptr(step_o), _ptr(step_lse), _ptr(workspace), ws_bytes,
                                _stream(stream)))
+
+
+def cp_ring_emulate_layout(shape, S, P, rank, chunks, q, k, v, doc, o, lse, dout=None, dq=None, dk=None, dv=None,
+                           workspace=None, stream=None):
+    """cp_ring_emulate under an explicit layout: ``chunks`` is a host int
+    sequence of P pairs (a, b), a < b (e.g. the first result of
+    cp_balanced_pairs); inputs are in that layout's sharded order."""
+    import numpy as np
+    lib = load()
+    _ring_checks(shape, S, P, rank, q, k, v, o, lse, dout, dq, dk, dv)
+    tab = np.ascontiguousarray(np.asarray(chunks, dtype=np.int32).reshape(-1))
+    if tab.size != 2 * P:
+        _arg_error(f"chunks holds {tab.size} entries, expected 2P={2 * P}")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.cp_ring_emulate_layout(ctypes.byref(shape), S, P, rank, tab.ctypes.data_as(ctypes.c_void_p),
+                                      _ptr(q), _ptr(k), _ptr(v), _ptr(doc), _ptr(o), _dtype_code(o), _ptr(lse),
+                                      _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+                                      _stream(stream)))
 
 
 def cp_ring_overlap_workspace_bytes(shape, S, P, o_dtype, backward):
@@ -225,6 +341,7 @@ def cp_ring_overlap_workspace_bytes(shape, S, P, o_dtype, backward):
 def cp_ring_emulate_overlap(shape, S, P, rank, q, k, v, doc, o, lse, dout=None, dq=None, dk=None, dv=None,
                             workspace=None, stream=None, copy_stream=None):
     lib = load()
+    _ring_checks(shape, S, P, rank, q, k, v, o, lse, dout, dq, dk, dv)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.cp_ring_emulate_overlap(ctypes.byref(shape), S, P, rank, _ptr(q), _ptr(k), _ptr(v), _ptr(doc),
                                        _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
@@ -239,6 +356,16 @@ def cp_ulysses_workspace_bytes(shape, S, sp, backward):
 def cp_ulysses_share(shape, S, sp, sp_rank, q, k, v, doc, o, lse, dout=None, dq=None, dk=None,
                      dv=None, workspace=None, stream=None):
     lib = load()
+    hq, hkv = shape.hq // sp, shape.hkv // sp
+    _tokens("q", q, shape.q_stride)
+    _tokens("k", k, shape.kv_stride)
+    _tokens("v", v, shape.kv_stride)
+    _dense("o", o, (S, hq, shape.d))
+    _dense("lse", lse, (hq, S))
+    _dense("dout", dout, (S, hq, shape.d))
+    _dense("dq", dq, (S, hq, shape.d))
+    _dense("dk", dk, (S, hkv, shape.d))
+    _dense("dv", dv, (S, hkv, shape.d))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.cp_ulysses_share(ctypes.byref(shape), S, sp, sp_rank, _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(doc), _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq),
@@ -252,6 +379,16 @@ def cp_allgather_workspace_bytes(shape, S, P, has_doc, backward):
 def cp_allgather_share(shape, S, P, rank, q, k, v, doc, o, lse, dout=None, dq=None, dk=None, dv=None,
                        workspace=None, stream=None):
     lib = load()
+    n = S // P
+    _tokens("q", q, shape.q_stride)
+    _tokens("k", k, shape.kv_stride)
+    _tokens("v", v, shape.kv_stride)
+    _dense("o", o, (n, shape.hq, shape.d))
+    _dense("lse", lse, (shape.hq, n))
+    _dense("dout", dout, (n, shape.hq, shape.d))
+    _dense("dq", dq, (n, shape.hq, shape.d))
+    _dense("dk", dk, (S, shape.hkv, shape.d))
+    _dense("dv", dv, (S, shape.hkv, shape.d))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.cp_allgather_share(ctypes.byref(shape), S, P, rank, _ptr(q), _ptr(k), _ptr(v), _ptr(doc),
                                   _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
@@ -264,6 +401,22 @@ def _host_doc(doc):
         return None, None
     d = np.ascontiguousarray(doc, dtype=np.int32)
     return d, d.ctypes.data_as(ctypes.c_void_p)
+
+
+def cp_check_docs(doc, stream=None):
+    """Checks document ids (>= 0, non-decreasing): ``doc`` is a GPU int32
+    tensor (copied to the host on the stream, which the call waits for) or a
+    host array.  Raises CpError (CP_ERR_DOCS) naming the first bad index."""
+    import numpy as np
+    lib = load()
+    if hasattr(doc, "is_cuda") and doc.is_cuda:
+        import torch
+        if doc.dtype != torch.int32 or not doc.is_contiguous():
+            _arg_error("doc must be a contiguous int32 tensor")
+        _check(lib.cp_check_docs(_ptr(doc), doc.numel(), 0, _stream(stream)))
+        return
+    d, dp = _host_doc(doc)
+    _check(lib.cp_check_docs(dp, 0 if d is None else d.size, 1, None))
 
 
 def cp_chunk_work(S, P, doc=None):

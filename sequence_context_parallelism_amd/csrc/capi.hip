@@ -64,6 +64,7 @@ cp_status check_shape(const cp_shape* sh) {
   if (!valid_dtype(sh->dtype)) return fail(CP_ERR_ARG, "unknown dtype %d", (int)sh->dtype);
   if (!(sh->scale > 0.f) || sh->scale != sh->scale) return fail(CP_ERR_ARG, "scale must be positive and finite");
   if (sh->causal != 0 && sh->causal != 1) return fail(CP_ERR_ARG, "causal must be 0 or 1");
+  if (sh->flags & ~CP_CHECK_DOCS) return fail(CP_ERR_ARG, "unknown flag bits 0x%x", (unsigned)sh->flags);
   const size_t esz = elt_size(sh->dtype);
   if (sh->q_stride < (int64_t)sh->hq * sh->d) return fail(CP_ERR_ARG, "q_stride %lld < hq*d", (long long)sh->q_stride);
   if (sh->kv_stride < (int64_t)sh->hkv * sh->d) return fail(CP_ERR_ARG, "kv_stride %lld < hkv*d", (long long)sh->kv_stride);
@@ -175,6 +176,47 @@ cp_status check_docs(const cp_span& a, const cp_span& b) {
   return CP_OK;
 }
 
+// Document ids must be >= 0 and non-decreasing in the order given (the mask
+// compares ids of equal value, and the kernels' tile classification reads a
+// tile's id range from its first and last token).
+cp_status validate_ids(const int32_t* h, int64_t n, const char* what) {
+  for (int64_t i = 0; i < n; ++i) {
+    if (h[i] < 0) return fail(CP_ERR_DOCS, "%s: doc id %d at index %lld is negative", what, h[i], (long long)i);
+    if (i > 0 && h[i] < h[i - 1])
+      return fail(CP_ERR_DOCS, "%s: doc ids decrease at index %lld (%d after %d)", what, (long long)i, h[i],
+                  h[i - 1]);
+  }
+  return CP_OK;
+}
+
+// A host copy of n device doc ids, taken on `st` (waits for the stream).
+cp_status fetch_ids(const int32_t* dev, int64_t n, hipStream_t st, std::vector<int32_t>& out) {
+  out.assign((size_t)n, 0);
+  if (n == 0) return CP_OK;
+  CP_TRY_HIP(hipMemcpyAsync(out.data(), dev, (size_t)n * 4, hipMemcpyDeviceToHost, st), "doc id copy");
+  CP_TRY_HIP(hipStreamSynchronize(st), "doc id copy");
+  return CP_OK;
+}
+
+bool checking_docs(const cp_shape* sh) { return (sh->flags & CP_CHECK_DOCS) != 0; }
+
+// CP_CHECK_DOCS for a chunk call: each span's ids in local order (which is
+// global order: positions increase along a span).
+cp_status check_span_ids(const cp_shape* sh, const cp_span& s, const char* name, hipStream_t st) {
+  if (!checking_docs(sh) || !s.doc) return CP_OK;
+  std::vector<int32_t> h;
+  CP_TRY(fetch_ids(s.doc, span_total(s), st, h));
+  return validate_ids(h.data(), (int64_t)h.size(), name);
+}
+
+// CP_CHECK_DOCS for a whole sequence held in global order.
+cp_status check_seq_ids(const cp_shape* sh, const int32_t* doc, int64_t S, hipStream_t st) {
+  if (!checking_docs(sh) || !doc) return CP_OK;
+  std::vector<int32_t> h;
+  CP_TRY(fetch_ids(doc, S, st, h));
+  return validate_ids(h.data(), S, "doc");
+}
+
 cp_status check_ptr(const void* p, const char* name) {
   if (!p) return fail(CP_ERR_ARG, "%s is NULL", name);
   if (!aligned16(p)) return fail(CP_ERR_ALIGN, "%s is not 16-byte aligned", name);
@@ -196,6 +238,46 @@ RingLayout ring_layout(const cp_shape* sh, int64_t n, cp_dtype o_dtype, bool bac
   L.delta = off; if (backward) off += lbytes;
   L.total = off;
   return L;
+}
+
+// The zigzag assignment as a chunk table: rank r holds chunks r and 2P-1-r.
+std::vector<int32_t> zigzag_pairs(int32_t P) {
+  std::vector<int32_t> t(2 * (size_t)P);
+  for (int32_t r = 0; r < P; ++r) {
+    t[2 * r] = r;
+    t[2 * r + 1] = 2 * P - 1 - r;
+  }
+  return t;
+}
+
+// A two-chunks-per-rank assignment: chunks[2r] < chunks[2r+1], every chunk
+// 0..2P-1 exactly once.
+cp_status check_pairs(const int32_t* chunks, int32_t P) {
+  if (!chunks) return fail(CP_ERR_ARG, "chunks is NULL");
+  std::vector<char> seen(2 * (size_t)P, 0);
+  for (int32_t r = 0; r < P; ++r) {
+    const int32_t a = chunks[2 * r], b = chunks[2 * r + 1];
+    if (a < 0 || b >= 2 * P || a >= b)
+      return fail(CP_ERR_ARG, "rank %d: chunks (%d, %d) must satisfy 0 <= a < b < 2P=%d", r, a, b, 2 * P);
+    if (seen[a] || seen[b]) return fail(CP_ERR_ARG, "rank %d: a chunk is assigned twice", r);
+    seen[a] = seen[b] = 1;
+  }
+  return CP_OK;
+}
+
+// CP_CHECK_DOCS for a ring: the ids come in sharded order; put them back in
+// global order under the chunk table and check that order.
+cp_status check_ring_ids(const cp_shape* sh, const int32_t* doc, int64_t S, int32_t P, const int32_t* pairs,
+                         hipStream_t st) {
+  if (!checking_docs(sh) || !doc) return CP_OK;
+  std::vector<int32_t> h, g((size_t)S);
+  CP_TRY(fetch_ids(doc, S, st, h));
+  const int64_t c = S / (2 * P), n = 2 * c;
+  for (int32_t r = 0; r < P; ++r)
+    for (int half = 0; half < 2; ++half)
+      std::copy(h.begin() + r * n + half * c, h.begin() + r * n + (half + 1) * c,
+                g.begin() + (int64_t)pairs[2 * r + half] * c);
+  return validate_ids(g.data(), S, "doc (global order)");
 }
 
 cp_status check_ring_args(const cp_shape* sh, int64_t S, int32_t P, int32_t rank) {
@@ -297,6 +379,8 @@ cp_status cp_attn_chunk_fwd(const cp_shape* sh, const void* q, cp_span qs, const
   CP_TRY(check_ptr(o, "o"));
   CP_TRY(check_ptr(lse, "lse"));
   if (Lk > 0) { CP_TRY(check_ptr(k, "k")); CP_TRY(check_ptr(v, "v")); }
+  CP_TRY(check_span_ids(sh, qs, "qs.doc", (hipStream_t)stream));
+  CP_TRY(check_span_ids(sh, ks, "ks.doc", (hipStream_t)stream));
   CP_TRY_HIP(run_fwd(sh, q, qs, k, v, ks, o, o_dtype, lse, Lq, (hipStream_t)stream), "cp_attn_chunk_fwd");
   return ok();
 }
@@ -347,6 +431,8 @@ static cp_status chunk_bwd(const cp_shape* sh, const void* q, cp_span qs, const 
     CP_TRY(check_ptr(dv, "dv"));
   }
   if (!lse || !delta) return fail(CP_ERR_ARG, "lse or delta is NULL");
+  CP_TRY(check_span_ids(sh, qs, "qs.doc", (hipStream_t)stream));
+  CP_TRY(check_span_ids(sh, ks, "ks.doc", (hipStream_t)stream));
   CP_TRY_HIP(run_bwd(sh, q, qs, k, v, ks, dout, lse, delta, Lq, dq, dk, dv, (hipStream_t)stream, part), name);
   return ok();
 }
@@ -410,12 +496,14 @@ size_t cp_ring_workspace_bytes(const cp_shape* sh, int64_t S, int32_t P, int32_t
 
 namespace {
 
-// The ring driver; with `ov` (a single rank, no per-step capture) the steps
-// read their KV shard from the receive area (see RingOverlap).
-cp_status ring_drive(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, const void* q, const void* k,
-                     const void* v, const int32_t* doc, void* o, cp_dtype o_dtype, float* lse, const void* dout,
-                     float* dq, float* dk, float* dv, float* step_o, float* step_lse, char* ws, hipStream_t st,
-                     const RingOverlap* ov) {
+// The ring driver.  Rank r holds chunks pairs[2r] < pairs[2r+1] (each of
+// S/(2P) tokens; the zigzag table, or a document-balanced one), so every
+// shard is a two-run span.  With `ov` (a single rank, no per-step capture)
+// the steps read their KV shard from the receive area (see RingOverlap).
+cp_status ring_drive(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, const int32_t* pairs, const void* q,
+                     const void* k, const void* v, const int32_t* doc, void* o, cp_dtype o_dtype, float* lse,
+                     const void* dout, float* dq, float* dk, float* dv, float* step_o, float* step_lse, char* ws,
+                     hipStream_t st, const RingOverlap* ov) {
   const bool backward = dout != nullptr;
   const int64_t n = S / P;                       // rows per rank = 2c
   const int32_t c = (int32_t)(S / (2 * P));
@@ -487,7 +575,8 @@ cp_status ring_drive(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, con
   for (int32_t r = r0; r < r1; ++r) {
     const int64_t out_row0 = rank < 0 ? (int64_t)r * n : 0;       // row offset into o / dq
     const char* qr = (const char*)q + (size_t)r * n * sh->q_stride * in_esz;
-    const cp_span qs = run_span((int64_t)r * c, c, (int64_t)(2 * P - 1 - r) * c, c, doc ? doc + r * n : nullptr);
+    const cp_span qs = run_span((int64_t)pairs[2 * r] * c, c, (int64_t)pairs[2 * r + 1] * c, c,
+                                doc ? doc + r * n : nullptr);
     char* o_r = (char*)o + (size_t)out_row0 * orow * o_esz;
     float* lse_r = lse + (rank < 0 ? (size_t)r * sh->hq * n : 0);
     float* acc_o = o_dtype == CP_F32 ? (float*)o_r : acc_o_ws;
@@ -498,7 +587,8 @@ cp_status ring_drive(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, con
       const cp_shape* shs;
       CP_TRY_HIP(prefetch(0, r, s), "ring receive copy");
       CP_TRY_HIP(step_kv(0, s, j, kj, vj, shs), "ring wait");
-      const cp_span ks = run_span((int64_t)j * c, c, (int64_t)(2 * P - 1 - j) * c, c, doc ? doc + j * n : nullptr);
+      const cp_span ks = run_span((int64_t)pairs[2 * j] * c, c, (int64_t)pairs[2 * j + 1] * c, c,
+                                  doc ? doc + j * n : nullptr);
       // bf16 steps after the first merge into the running result in the
       // forward kernel's epilogue (no partial round trip through HBM)
       if (s > 0 && !step_o && sh->dtype == CP_BF16) {
@@ -536,7 +626,8 @@ cp_status ring_drive(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, con
         const cp_shape* shs;
         CP_TRY_HIP(prefetch(1, r, s), "ring receive copy");
         CP_TRY_HIP(step_kv(1, s, j, kj, vj, shs), "ring wait");
-        const cp_span ks = run_span((int64_t)j * c, c, (int64_t)(2 * P - 1 - j) * c, c, doc ? doc + j * n : nullptr);
+        const cp_span ks = run_span((int64_t)pairs[2 * j] * c, c, (int64_t)pairs[2 * j + 1] * c, c,
+                                    doc ? doc + j * n : nullptr);
         float* dkj = dk + (size_t)j * n * kvrow;
         float* dvj = dv + (size_t)j * n * kvrow;
         if (!ov) {
@@ -579,8 +670,23 @@ cp_status cp_ring_emulate(const cp_shape* sh, int64_t S, int32_t P, int32_t rank
   if (step_o && rank < 0) return fail(CP_ERR_ARG, "per-step capture needs a single rank");
   if (step_o) CP_TRY(check_ptr(step_o, "step_o"));
   CP_TRY(check_workspace(workspace, ws_bytes, ring_layout(sh, S / P, o_dtype, dout != nullptr).total));
-  return ring_drive(sh, S, P, rank, q, k, v, doc, o, o_dtype, lse, dout, dq, dk, dv, step_o, step_lse,
-                    (char*)workspace, (hipStream_t)stream, nullptr);
+  const std::vector<int32_t> pairs = zigzag_pairs(P);
+  CP_TRY(check_ring_ids(sh, doc, S, P, pairs.data(), (hipStream_t)stream));
+  return ring_drive(sh, S, P, rank, pairs.data(), q, k, v, doc, o, o_dtype, lse, dout, dq, dk, dv, step_o,
+                    step_lse, (char*)workspace, (hipStream_t)stream, nullptr);
+}
+
+cp_status cp_ring_emulate_layout(const cp_shape* sh, int64_t S, int32_t P, int32_t rank, const int32_t* chunks,
+                                 const void* q, const void* k, const void* v, const int32_t* doc, void* o,
+                                 cp_dtype o_dtype, float* lse, const void* dout, float* dq, float* dk, float* dv,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  CP_TRY(ring_args(sh, S, P, rank, q, k, v, o, o_dtype, lse, dout, dq, dk, dv));
+  CP_TRY(check_pairs(chunks, P));
+  CP_TRY(check_workspace(workspace, ws_bytes, ring_layout(sh, S / P, o_dtype, dout != nullptr).total));
+  const std::vector<int32_t> pairs(chunks, chunks + 2 * (size_t)P);     // the host table, copied once
+  CP_TRY(check_ring_ids(sh, doc, S, P, pairs.data(), (hipStream_t)stream));
+  return ring_drive(sh, S, P, rank, pairs.data(), q, k, v, doc, o, o_dtype, lse, dout, dq, dk, dv, nullptr,
+                    nullptr, (char*)workspace, (hipStream_t)stream, nullptr);
 }
 
 size_t cp_ring_overlap_workspace_bytes(const cp_shape* sh, int64_t S, int32_t P, cp_dtype o_dtype, int32_t backward) {
@@ -604,8 +710,10 @@ cp_status cp_ring_emulate_overlap(const cp_shape* sh, int64_t S, int32_t P, int3
   CP_TRY(check_workspace(workspace, ws_bytes, L.total));
   char* ws = (char*)workspace;
   RingOverlap ov{(hipStream_t)copy_stream, {ws + L.recv0, ws + L.recv1}, (float*)(ws + L.send)};
-  return ring_drive(sh, S, P, rank, q, k, v, doc, o, o_dtype, lse, dout, dq, dk, dv, nullptr, nullptr, ws,
-                    (hipStream_t)stream, &ov);
+  const std::vector<int32_t> pairs = zigzag_pairs(P);
+  CP_TRY(check_ring_ids(sh, doc, S, P, pairs.data(), (hipStream_t)stream));
+  return ring_drive(sh, S, P, rank, pairs.data(), q, k, v, doc, o, o_dtype, lse, dout, dq, dk, dv, nullptr,
+                    nullptr, ws, (hipStream_t)stream, &ov);
 }
 
 size_t cp_ulysses_workspace_bytes(const cp_shape* sh, int64_t S, int32_t sp, int32_t backward) {
@@ -650,6 +758,7 @@ cp_status cp_ulysses_share(const cp_shape* sh_full, int64_t S, int32_t sp, int32
   if (!aligned16(qs_ptr) || !aligned16(ks_ptr)) return fail(CP_ERR_ALIGN, "head slice not 16-byte aligned");
   const cp_span span = run_span(0, (int32_t)S, S, 0, doc);
   hipStream_t st = (hipStream_t)stream;
+  CP_TRY(check_seq_ids(sh_full, doc, S, st));
   CP_TRY_HIP(run_fwd(&sh, qs_ptr, span, ks_ptr, vs_ptr, span, o, o_dtype, lse, S, st), "ulysses forward");
   if (backward) {
     float* dlt = (float*)workspace;
@@ -736,6 +845,7 @@ cp_status cp_allgather_share(const cp_shape* sh, int64_t S, int32_t P, int32_t r
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(CP_ERR_ALIGN, "workspace must be 256-byte aligned");
   }
   hipStream_t st = (hipStream_t)stream;
+  CP_TRY(check_seq_ids(sh, doc, S, st));
   const int64_t n = S / P;
   const int32_t c = (int32_t)(S / (2 * P));
   char* ws = (char*)workspace;
@@ -759,6 +869,20 @@ cp_status cp_allgather_share(const cp_shape* sh, int64_t S, int32_t P, int32_t r
     CP_TRY_HIP(run_bwd(sh, q, qs, k, v, ks, dout, lse, dlt, n, dq, dk, dv, st, BWD_ALL, true),
                "all-gather backward");
   }
+  return ok();
+}
+
+cp_status cp_check_docs(const int32_t* doc, int64_t n, int32_t on_host, void* stream) {
+  if (n < 0) return fail(CP_ERR_ARG, "n=%lld is negative", (long long)n);
+  if (n == 0) return ok();
+  if (!doc) return fail(CP_ERR_ARG, "doc is NULL");
+  if (on_host) {
+    CP_TRY(validate_ids(doc, n, "doc"));
+    return ok();
+  }
+  std::vector<int32_t> h;
+  CP_TRY(fetch_ids(doc, n, (hipStream_t)stream, h));
+  CP_TRY(validate_ids(h.data(), n, "doc"));
   return ok();
 }
 
@@ -808,6 +932,8 @@ cp_status cp_tile_map(const cp_shape* sh, cp_span qs, cp_span ks, int32_t bq, in
   if (bq <= 0 || bk <= 0) return fail(CP_ERR_ARG, "tile sizes must be positive");
   if (span_total(qs) == 0 || span_total(ks) == 0) return ok();
   if (!out) return fail(CP_ERR_ARG, "out is NULL");
+  CP_TRY(check_span_ids(sh, qs, "qs.doc", (hipStream_t)stream));
+  CP_TRY(check_span_ids(sh, ks, "ks.doc", (hipStream_t)stream));
   CP_TRY_HIP(launch_tile_map(to_dev(qs), to_dev(ks), sh->causal, bq, bk, out, (hipStream_t)stream),
              "cp_tile_map");
   return ok();

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(cp.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert cp.cp_abi_version() == 1
+    assert cp.cp_abi_version() == 2
 
 
 @pytest.mark.parametrize("S,P", [(16, 2), (256, 2), (131072, 8), (1048576, 4), (96, 6), (8, 1)])
@@ -195,3 +195,57 @@ def test_chunk_work_rejects_bad_docs(lib):
         cp.cp_chunk_work(8, 2, np.array([0, 0, 1, 0, 1, 1, 1, 1], dtype=np.int32))
     with pytest.raises(cp.CpError):
         cp.cp_chunk_work(10, 2)
+
+
+# ---- document ids (Llama 3 page, section "네 병렬화는 서로 다른 자원을 확보하는
+# 방식": packed documents must keep their mask) ----------------------------------
+
+@pytest.mark.parametrize("ids,ok", [
+    ([0, 0, 1, 1, 5, 5, 9], True),
+    ([], True),
+    ([3], True),
+    ([0, 0, -1, 2], False),          # negative
+    ([-4, -4, -4], False),
+    ([0, 1, 2, 1, 3], False),        # decreasing
+    ([5, 4], False),
+])
+def test_check_docs_on_host_copy(lib, ids, ok):
+    arr = np.array(ids, dtype=np.int32)
+    if ok:
+        cp.cp_check_docs(arr)
+    else:
+        with pytest.raises(cp.CpError) as e:
+            cp.cp_check_docs(arr)
+        assert e.value.status == cp.CP_ERR_DOCS
+        assert "index" in lib.cp_last_error().decode()
+
+
+def test_check_docs_argument_errors(lib):
+    assert lib.cp_check_docs(None, 4, 1, None) == cp.CP_ERR_ARG
+    assert lib.cp_check_docs(None, -1, 1, None) == cp.CP_ERR_ARG
+    assert lib.cp_check_docs(None, 0, 1, None) == cp.CP_OK
+
+
+def test_unknown_flag_bits_are_refused(lib):
+    assert _fwd_status(lib, _shape(flags=2)) == cp.CP_ERR_ARG
+    # the one defined bit passes the shape check (an empty query span then returns before any launch)
+    assert _fwd_status(lib, _shape(flags=cp.CP_CHECK_DOCS), qs=cp.make_span(0, 0)) == cp.CP_OK
+
+
+@pytest.mark.parametrize("chunks,status", [
+    ([0, 7, 1, 6, 2, 5, 3, 4], cp.CP_ERR_WORKSPACE),      # zigzag table: valid, then the missing workspace
+    ([0, 1, 2, 3, 4, 5, 6, 7], cp.CP_ERR_WORKSPACE),      # any pairing with a < b is valid
+    ([1, 0, 2, 3, 4, 5, 6, 7], cp.CP_ERR_ARG),            # a > b
+    ([0, 1, 1, 2, 4, 5, 6, 7], cp.CP_ERR_ARG),            # chunk 1 twice
+    ([0, 1, 2, 3, 4, 5, 6, 8], cp.CP_ERR_ARG),            # out of range
+])
+def test_ring_layout_table_checks(lib, chunks, status):
+    sh = _shape()
+    P = ctypes.c_void_p(0x10000)
+    tab = np.array(chunks, dtype=np.int32)
+    st = lib.cp_ring_emulate_layout(ctypes.byref(sh), 1024, 4, 0, tab.ctypes.data_as(ctypes.c_void_p),
+                                    P, P, P, None, P, cp.CP_BF16, P, None, None, None, None, None, 0, None)
+    assert st == status, lib.cp_last_error().decode()
+    st = lib.cp_ring_emulate_layout(ctypes.byref(sh), 1024, 4, 0, None, P, P, P, None, P, cp.CP_BF16, P,
+                                    None, None, None, None, None, 0, None)
+    assert st == cp.CP_ERR_ARG

@@ -286,3 +286,87 @@ def test_ring_single_rank_is_plain_causal_attention(gpu_lib):
     assert max_abs(host(dq), rdq) <= grad_tol(rdq, tol["grad"])
     assert max_abs(host(dk), rdk) <= grad_tol(rdk, tol["grad"])
     assert max_abs(host(dv), rdv) <= grad_tol(rdv, tol["grad"])
+
+
+def _layout_case(S, P, seed):
+    """Packed documents and the document-balanced pairing of their chunks."""
+    lens = cpinputs.lognormal_doc_lengths(S, seed=seed, median=S // 10, sigma=1.0, lo=8, hi=S)
+    doc_g = cpinputs.doc_ids_from_lengths(lens)
+    pairs, _ = cp.cp_balanced_pairs(S, P, doc_g)
+    return doc_g, [tuple(int(x) for x in p) for p in pairs]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("layout", ["balanced", "fixed"])
+def test_ring_layout_one_rank_matches_oracle(gpu_lib, dtype, layout):
+    """The ring under a non-zigzag two-chunk layout (the document-balanced
+    pairing of cp_balanced_pairs, or a fixed table): one rank's O, LSE, dQ and
+    dK/dV contributions against the oracle's ring over the same layout."""
+    S, P, hq, hkv, d = 1536, 4, 8, 2, 128
+    doc_g, chunks = _layout_case(S, P, 91)
+    if layout == "fixed":
+        chunks = [(0, 1), (2, 5), (3, 4), (6, 7)]
+    zz = [(r, 2 * P - 1 - r) for r in range(P)]
+    assert sorted(chunks) != sorted(zz), "the case must differ from zigzag"
+    order = Z.sharded_order(S, P, chunks)
+    doc = doc_g[order]                                    # ids in this layout's sharded order
+    print(f"ring layout {layout} {dtype}: chunks {chunks}", flush=True)
+    (qh, kh, vh, doh), (qd, kd, vd, dod) = inputs(4400, [(S, hq, d), (S, hkv, d), (S, hkv, d), (S, hq, d)], dtype)
+    doc_d = torch.from_numpy(doc).to(DEV)
+    sh = shape_for(hq, hkv, d, dtype)
+    n = S // P
+    tol = TOL[dtype]
+    for r in (0, P - 1):
+        nan = float("nan")
+        o = torch.full((n, hq, d), nan, device=DEV, dtype=dtype)
+        lse = torch.full((hq, n), nan, device=DEV)
+        dq = torch.full((n, hq, d), nan, device=DEV)
+        dk = torch.full((S, hkv, d), nan, device=DEV)
+        dv = torch.full_like(dk, nan)
+        dout = dod[r * n:(r + 1) * n]
+        ws = cp.workspace(cp.cp_ring_workspace_bytes(sh, S, P, r, sh.dtype, True))
+        cp.cp_ring_emulate_layout(sh, S, P, r, chunks, qd, kd, vd, doc_d, o, lse, dout, dq, dk, dv, workspace=ws)
+        torch.cuda.synchronize()
+        ro, rl, _ = Z.ring_forward(qh, kh, vh, S, P, r, scale=sh.scale, doc=doc, chunks=chunks)
+        assert max_abs(host(o), ro) <= tol["o"]
+        assert lse_err(host(lse), rl) <= tol["lse"]
+        rdq, rdk, rdv = Z.ring_backward(qh, kh, vh, doh[r * n:(r + 1) * n], ro, rl, S, P, r,
+                                        scale=sh.scale, doc=doc, chunks=chunks)
+        assert max_abs(host(dq), rdq) <= grad_tol(rdq, tol["grad"])
+        assert max_abs(host(dk), rdk) <= grad_tol(rdk, tol["grad"])
+        assert max_abs(host(dv), rdv) <= grad_tol(rdv, tol["grad"])
+
+
+def test_ring_balanced_layout_all_ranks_is_full_attention(gpu_lib):
+    """Every rank of the document-balanced ring together: the outputs, in
+    that layout's sharded order, equal plain document-masked causal
+    attention over the sequence, and dK/dV are the full gradients."""
+    S, P, hq, hkv, d = 2048, 4, 4, 2, 128
+    dtype = torch.bfloat16
+    doc_g, chunks = _layout_case(S, P, 93)
+    order = Z.sharded_order(S, P, chunks)
+    print(f"ring balanced all ranks: chunks {chunks}", flush=True)
+    (qg, kg, vg, dog), _ = inputs(4500, [(S, hq, d), (S, hkv, d), (S, hkv, d), (S, hq, d)], dtype)
+    qd, kd, vd, dod = (torch.from_numpy(x[order].astype(np.float32)).to(DEV).to(dtype) for x in (qg, kg, vg, dog))
+    doc_d = torch.from_numpy(doc_g[order]).to(DEV)
+    sh = shape_for(hq, hkv, d, dtype)
+    n = S // P
+    o = torch.empty(S, hq, d, device=DEV, dtype=dtype)
+    lse = torch.empty(P, hq, n, device=DEV)
+    dq = torch.empty(S, hq, d, device=DEV)
+    dk = torch.empty(S, hkv, d, device=DEV)
+    dv = torch.empty_like(dk)
+    ws = cp.workspace(cp.cp_ring_workspace_bytes(sh, S, P, -1, cp.CP_BF16, True))
+    cp.cp_ring_emulate_layout(sh, S, P, -1, chunks, qd, kd, vd, doc_d, o, lse, dod, dq, dk, dv, workspace=ws)
+    torch.cuda.synchronize()
+    pos = np.arange(S)
+    ro, rl = A.forward(qg, kg, vg, pos, pos, scale=sh.scale, causal=True, qdoc=doc_g, kdoc=doc_g)
+    rdq, rdk, rdv = A.backward(qg, kg, vg, dog, rl, A.delta(ro, dog), pos, pos, scale=sh.scale, causal=True,
+                               qdoc=doc_g, kdoc=doc_g)
+    tol = TOL[dtype]
+    assert max_abs(host(o), ro[order]) <= tol["o"]
+    gl = host(lse).transpose(1, 0, 2).reshape(hq, S)
+    assert lse_err(gl, rl[:, order]) <= tol["lse"]
+    assert max_abs(host(dq), rdq[order]) <= grad_tol(rdq, tol["grad"])
+    assert max_abs(host(dk), rdk[order]) <= grad_tol(rdk, tol["grad"])
+    assert max_abs(host(dv), rdv[order]) <= grad_tol(rdv, tol["grad"])
