@@ -15,7 +15,10 @@ fp64 oracle timed on the host cores on a bounded sample.
 Other workloads (``--workload``): ring_128k (rank 0 of a zigzag ring of
 P=8 over S=131072, 32/8 heads), docs_128k (S=131072 packed lognormal
 documents, 32/8 heads), usp_1m (rank 0 of a 4-rank ring over S=1,048,576 for
-an 8/2 head slice).
+an 8/2 head slice).  The default run also carries a ``workloads`` object with
+a short run of each of them (1 warm-up, 2 timed steps, medians), and for the
+packed documents the per-rank time of a P=8 ring under the zigzag layout and
+under the document-balanced pairing.
 """
 from __future__ import annotations
 
@@ -44,6 +47,8 @@ def parse():
                     choices=["ulysses_64k", "ring_128k", "docs_128k", "usp_1m"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="with the default workload, skip the short runs of the other workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (3 times), the reference for "
                          "scaling HBM traffic counters")
@@ -165,29 +170,31 @@ def kernel_times(wl, cp, torch, iters):
     o32 = torch.empty(wl.rows, wl.hq, wl.d, device=wl.dev)
     lse2 = torch.empty_like(wl.lse)
     o_part = torch.empty_like(o32)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    # the forward as the step runs it: a single-chunk share writes its final
+    # bf16 output; a ring step writes an fp32 partial
+    o_fwd = o32 if wl.name in ("ring_128k", "usp_1m") else wl.o
     cp.cp_attn_chunk_fwd(wl.sh, wl.q, qs, k, v, ks, wl.o, wl.lse)
     cp.cp_attn_delta(wl.o, wl.dout, wl.delta)
     cp.cp_attn_chunk_fwd(wl.sh, wl.q, qs, k, v, ks, o_part, lse2)
     torch.cuda.synchronize()
-    ev[0].record(st)
-    for _ in range(iters):
-        cp.cp_attn_chunk_fwd(wl.sh, wl.q, qs, k, v, ks, o32, lse2)
-    ev[1].record(st)
-    for _ in range(iters):
-        cp.cp_attn_chunk_bwd_dkdv(wl.sh, wl.q, qs, k, v, ks, wl.dout, wl.lse, wl.delta, dk, dv)
-    ev[2].record(st)
-    for _ in range(iters):
-        cp.cp_attn_chunk_bwd_dq(wl.sh, wl.q, qs, k, v, ks, wl.dout, wl.lse, wl.delta, wl.dq)
-    ev[3].record(st)
-    for _ in range(iters):      # merge a partial into an accumulator of the output's shape
-        cp.cp_lse_merge(o32, lse2, o_part, wl.lse)
-    ev[4].record(st)
-    for _ in range(iters):      # the backward's Delta = rowsum(dO * O) of the final output
-        cp.cp_attn_delta(wl.o, wl.dout, wl.delta)
-    ev[5].record(st)
-    torch.cuda.synchronize()
-    ms = [ev[i].elapsed_time(ev[i + 1]) / iters for i in range(5)]
+    launches = [
+        lambda: cp.cp_attn_chunk_fwd(wl.sh, wl.q, qs, k, v, ks, o_fwd, lse2),
+        lambda: cp.cp_attn_chunk_bwd_dkdv(wl.sh, wl.q, qs, k, v, ks, wl.dout, wl.lse, wl.delta, dk, dv),
+        lambda: cp.cp_attn_chunk_bwd_dq(wl.sh, wl.q, qs, k, v, ks, wl.dout, wl.lse, wl.delta, wl.dq),
+        lambda: cp.cp_lse_merge(o32, lse2, o_part, wl.lse),       # a partial into an accumulator
+        lambda: cp.cp_attn_delta(wl.o, wl.dout, wl.delta),        # Delta = rowsum(dO * O), final output
+    ]
+    ms, med = [], []
+    for fn in launches:         # each launch bracketed by events on the stream it runs on
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        ev[0].record(st)
+        for i in range(iters):
+            fn()
+            ev[i + 1].record(st)
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(iters)]
+        ms.append(sum(per) / iters)
+        med.append(float(np.median(per)))
     rh = wl.rows * wl.hq
     extra = {}
     if wl.name == "ulysses_64k":
@@ -219,11 +226,13 @@ def kernel_times(wl, cp, torch, iters):
     # recomputes S and dP (executed, not algorithmic).
     unit = 2 * wl.d * pairs * wl.hq
     return {
-        "fwd_bf16_kernel": {"ms": ms[0], "flops": 2 * unit, "flops_executed": 2 * unit},
-        "dkdv_bf16_kernel": {"ms": ms[1], "flops": 4 * unit, "flops_executed": 4 * unit},
-        "dq_bf16_kernel": {"ms": ms[2], "flops": 1 * unit, "flops_executed": 3 * unit},
-        "merge_kernel": {"ms": ms[3], "bytes": rh * (3 * wl.d * 4 + 3 * 4)},
-        "delta_kernel": {"ms": ms[4], "bytes": rh * (2 * wl.d * 2 + 4)},   # read O, dO (bf16), write Delta
+        "fwd_bf16_kernel": {"ms": ms[0], "ms_median": med[0], "flops": 2 * unit, "flops_executed": 2 * unit,
+                            "o_dtype": "f32" if o_fwd is o32 else "bf16"},
+        "dkdv_bf16_kernel": {"ms": ms[1], "ms_median": med[1], "flops": 4 * unit, "flops_executed": 4 * unit},
+        "dq_bf16_kernel": {"ms": ms[2], "ms_median": med[2], "flops": 1 * unit, "flops_executed": 3 * unit},
+        "merge_kernel": {"ms": ms[3], "ms_median": med[3], "bytes": rh * (3 * wl.d * 4 + 3 * 4)},
+        # read O, dO (bf16), write Delta
+        "delta_kernel": {"ms": ms[4], "ms_median": med[4], "bytes": rh * (2 * wl.d * 2 + 4)},
         **extra,
     }
 
@@ -319,17 +328,34 @@ def cpu_baseline(wl):
             cores = min(cores, max(blas))
     except Exception:
         pass
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
-    except OSError:
-        pass
+    model = cpu_model()
     return {"value": flops / t / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
             "sample": f"fp64 numpy oracle, forward+backward of one KV group ({g} query heads) over the "
                       f"first {L} tokens, causal; {t:.1f} s",
-            "seconds": t, "pairs_per_s": pairs / t, "gflops_fp64": flops / t / 1e9, "cpu_model": model,
+            "seconds": t, "pairs_per_s": pairs / t, "gflops_fp64": flops / t / 1e9, "cpu_model": model["name"],
+            "cpu_id": model["id"], "cpu_logical_cpus": model["logical"],
             "torch_threads": torch.get_num_threads()}
+
+
+def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family/model/stepping
+    numbers (some hosts report only a short marketing name)."""
+    info = {}
+    n = 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ":" not in ln:
+                    continue
+                key, val = (x.strip() for x in ln.split(":", 1))
+                if key == "processor":
+                    n += 1
+                info.setdefault(key, val)
+    except OSError:
+        pass
+    ident = " ".join(f"{k.replace('cpu ', '')} {info[k]}" for k in ("vendor_id", "cpu family", "model", "stepping")
+                     if k in info)
+    return {"name": info.get("model name", ""), "id": ident, "logical": n}
 
 
 XGMI_LINK_GBS = 153.0   # one xGMI link, per direction (the ring's neighbour link)
@@ -394,6 +420,96 @@ def allgather_share(wl, cp, torch, steps, ms_ring):
             "vs_ring_step": round(ms / ms_ring, 4)}
 
 
+def timed_steps(fn, torch, warmup, steps):
+    """Per-step milliseconds of `steps` calls after `warmup`, each bracketed by
+    events on the current stream."""
+    st = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(st)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(st)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def layout_rows(S, P, pairs):
+    """Global row of every row of a sharded-order array when rank r holds
+    chunks pairs[r] = (a, b): rank 0's two chunks first, then rank 1's."""
+    c = S // (2 * P)
+    return np.concatenate([np.arange(x * c, (x + 1) * c) for a, b in pairs for x in (a, b)])
+
+
+def ring_balance_timing(wl, cp, torch, P=8, passes=2):
+    """Per-rank time of a ring over the packed documents (forward +
+    backward of each rank's share, every rank run in turn on this GPU), for
+    the zigzag layout and for the document-balanced pairing of
+    cp_balanced_pairs.  The ids are put in each layout's sharded order; the
+    random Q/K/V rows need no reordering for timing."""
+    S, hq, hkv, d = wl.S, wl.hq, wl.hkv, wl.d
+    n = S // P
+    doc_g = wl.doc.cpu().numpy()
+    work = cp.cp_chunk_work(S, P, doc_g)
+    zz = [(r, 2 * P - 1 - r) for r in range(P)]
+    bal, _ = cp.cp_balanced_pairs(S, P, doc_g)
+    bal = [tuple(int(x) for x in p) for p in bal]
+    lse = torch.empty(hq, n, device=wl.dev)
+    o, dq, dout = wl.o[:n], wl.dq[:n], wl.dout[:n]
+    ws = cp.workspace(max(cp.cp_ring_workspace_bytes(wl.sh, S, P, r, cp.CP_BF16, True) for r in range(P)))
+    res = {"P": P}
+    for name, pairs in (("zigzag", zz), ("doc_balanced", bal)):
+        doc = torch.from_numpy(np.ascontiguousarray(doc_g[layout_rows(S, P, pairs)])).to(wl.dev)
+        rank_ms = []
+        for r in range(P):
+            def run(r=r):
+                cp.cp_ring_emulate_layout(wl.sh, S, P, r, pairs, wl.q, wl.k, wl.v, doc, o, lse, dout, dq,
+                                          wl.dk, wl.dv, workspace=ws)
+            rank_ms.append(float(np.median(timed_steps(run, torch, 1, passes))))
+        w = np.array([work[a] + work[b] for a, b in pairs], dtype=np.float64)
+        t = np.array(rank_ms)
+        res[name] = {"chunks": [list(p) for p in pairs], "rank_ms": [round(x, 3) for x in rank_ms],
+                     "max_over_mean_ms": round(float(t.max() / t.mean()), 3),
+                     "max_over_mean_work": round(float(w.max() / w.mean()), 3),
+                     "busiest_rank_ms": round(float(t.max()), 3)}
+    res["busiest_rank_speedup"] = round(res["zigzag"]["busiest_rank_ms"] / res["doc_balanced"]["busiest_rank_ms"], 3)
+    return res
+
+
+def other_workloads(head_wl, cp, torch, cpinputs, warmup=1, steps=2):
+    """Short runs of the other workloads (ring rank of P=8 over 128K tokens,
+    packed documents over 128K, the USP share over 1M tokens): warmup + steps
+    calls each, per-step medians.  The packed-document entry also carries the
+    per-rank ring timing of the zigzag and document-balanced layouts."""
+    out = {}
+    for name in ("ring_128k", "docs_128k", "usp_1m"):
+        torch.cuda.empty_cache()
+        wl = Workload(name, torch, cp, cpinputs)
+        torch.cuda.synchronize()
+        print(f"[bench] workload {name} ready", file=sys.stderr, flush=True)
+        per = timed_steps(lambda: wl.step(cp), torch, warmup, steps)
+        ms = float(np.median(per))
+        flops = wl.flops_fwd + wl.flops_bwd
+        tf = flops / (ms * 1e-3) / 1e12
+        e = {"config": wl.config, "steps": steps, "warmup": warmup, "ms_per_step_median": round(ms, 3),
+             "ms_per_step": [round(x, 3) for x in per], "tflops": round(tf, 1),
+             "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+             "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1),
+             "tokens_per_s_per_gpu": round(wl.tokens / (ms * 1e-3) / wl.group, 1),
+             "flops_per_step": flops}
+        print(f"[bench] {name}: {ms:.2f} ms/step, {tf:.1f} TFLOPS", file=sys.stderr, flush=True)
+        if name == "docs_128k":
+            e["ring_balance"] = ring_balance_timing(wl, cp, torch)
+            print(f"[bench] docs_128k ring balance: {e['ring_balance']['busiest_rank_speedup']}x on the busiest "
+                  "rank", file=sys.stderr, flush=True)
+        out[name] = e
+        del wl
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -425,16 +541,17 @@ def main():
         wl.step(cp)
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    e0.record(st)
-    for _ in range(args.steps):
+    evs[0].record(st)
+    for i in range(args.steps):
         wl.step(cp)
-    e1.record(st)
+        evs[i + 1].record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    ms_med = float(np.median([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]))
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
     parity = sampled_parity(wl, torch)
 
@@ -443,6 +560,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(ms_med, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": wl.config,
@@ -459,6 +577,10 @@ def main():
         out["kernels"] = {}
         for name, r in kt.items():
             e = {"ms": round(r["ms"], 4)}
+            if "ms_median" in r:
+                e["ms_median"] = round(r["ms_median"], 4)
+            if "o_dtype" in r:
+                e["o_dtype"] = r["o_dtype"]
             if "flops" in r:
                 e["tflops"] = round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 1)
                 e["tflops_executed"] = round(r["flops_executed"] / (r["ms"] * 1e-3) / 1e12, 1)
@@ -500,6 +622,8 @@ def main():
         out["allgather_share"] = allgather_share(wl, cp, torch, max(1, min(args.steps, 3)), ms)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
+    if args.workload == "ulysses_64k" and not args.no_workloads:
+        out["workloads"] = other_workloads(wl, cp, torch, cpinputs)
     print(json.dumps(out), flush=True)
 
 

@@ -64,3 +64,18 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "--gpus 2 is not supported" in r.stderr
+
+
+def test_bench_layout_rows_match_the_oracle_sharded_order():
+    """bench.py puts document ids into a layout's sharded order with its own
+    small helper; it must agree with the oracle's definition."""
+    from oracle import schedule as Z
+    for S, P, pairs in ((64, 2, [(0, 3), (1, 2)]), (96, 3, [(0, 1), (2, 5), (3, 4)]),
+                        (128, 4, [(0, 4), (1, 7), (3, 5), (2, 6)])):
+        assert bench.layout_rows(S, P, pairs).tolist() == Z.sharded_order(S, P, pairs).tolist()
+
+
+def test_bench_cpu_model_fields():
+    m = bench.cpu_model()
+    assert set(m) == {"name", "id", "logical"}
+    assert m["logical"] >= 1
