@@ -274,6 +274,28 @@ cp_status cp_ulysses_share(const cp_shape *sh_full, int64_t S, int32_t sp, int32
                            const void *dout, float *dq, float *dk, float *dv,
                            void *workspace, size_t ws_bytes, void *stream);
 
+/* Size of the device scratch built into the library for
+ * cp_ulysses_share_noalloc (per GPU, held until the process ends). */
+#define CP_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* cp_ulysses_share for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and results, bitwise, without the workspace.  The
+ * backward's Delta rows ((hq/sp) * S fp32) go to a scratch array built into
+ * the library, CP_NOALLOC_SCRATCH_BYTES per GPU; larger shares get
+ * CP_ERR_WORKSPACE.  The call allocates nothing (no hipMalloc, no library
+ * allocation); the scratch's device address is looked up once per GPU on the
+ * first call there.  Every call on one GPU shares that GPU's scratch: calls
+ * that overlap on one GPU (different streams, or threads) race and must be
+ * ordered by the caller.  Delta is written in full before it is read, so
+ * nothing depends on what an earlier call left there.  CP_CHECK_DOCS is
+ * refused (CP_ERR_ARG): it copies ids to the host and waits; run
+ * cp_check_docs beforehand instead. */
+cp_status cp_ulysses_share_noalloc(const cp_shape *sh_full, int64_t S, int32_t sp, int32_t sp_rank,
+                                   const void *q, const void *k, const void *v, const int32_t *doc,
+                                   void *o, cp_dtype o_dtype, float *lse,
+                                   const void *dout, float *dq, float *dk, float *dv, void *stream);
+
 /* Workspace bytes cp_allgather_share needs (0 on bad args). */
 size_t cp_allgather_workspace_bytes(const cp_shape *sh, int64_t S, int32_t P, int32_t has_doc, int32_t backward);
 

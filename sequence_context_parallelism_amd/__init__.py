@@ -27,7 +27,8 @@ EXPORTED = (
     "cp_zigzag_layout", "cp_ring_schedule", "cp_ring_workspace_bytes", "cp_ring_emulate",
     "cp_ring_emulate_layout",
     "cp_ring_overlap_workspace_bytes", "cp_ring_emulate_overlap",
-    "cp_ulysses_workspace_bytes", "cp_ulysses_share", "cp_allgather_workspace_bytes", "cp_allgather_share",
+    "cp_ulysses_workspace_bytes", "cp_ulysses_share", "cp_ulysses_share_noalloc",
+    "cp_allgather_workspace_bytes", "cp_allgather_share",
     "cp_check_docs", "cp_chunk_work", "cp_balanced_pairs",
     "cp_a2a_tokens_to_heads", "cp_a2a_heads_to_tokens",
     "cp_tile_map", "cp_last_error", "cp_abi_version",
@@ -87,6 +88,7 @@ def load(path: str = LIB_PATH):
         "cp_ulysses_workspace_bytes": (SZ, [SH, I64, I32, I32]),
         "cp_ulysses_share": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, P,
                                    SZ, P]),
+        "cp_ulysses_share_noalloc": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, P]),
         "cp_allgather_workspace_bytes": (SZ, [SH, I64, I32, I32, I32]),
         "cp_allgather_share": (I32, [SH, I64, I32, I32, P, P, P, P, P, I32, P, P, P, P, P, P, SZ, P]),
         "cp_check_docs": (I32, [P, I64, I32, P]),
@@ -127,10 +129,12 @@ def _dense(name, t, shape=None):
         return
     if not t.is_cuda:
         _arg_error(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        _arg_error(f"{name} must be contiguous (shape {tuple(t.shape)}, strides {tuple(t.stride())})")
     if shape is not None and tuple(t.shape) != tuple(shape):
         _arg_error(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.numel() == 0:
+        return
+    if not t.is_contiguous():
+        _arg_error(f"{name} must be contiguous (shape {tuple(t.shape)}, strides {tuple(t.stride())})")
 
 
 def _tokens(name, t, stride):
@@ -140,6 +144,8 @@ def _tokens(name, t, stride):
         return
     if not t.is_cuda:
         _arg_error(f"{name} must be a GPU tensor")
+    if t.numel() == 0:                     # an empty span: nothing is read
+        return
     if t.dim() >= 2 and t.shape[0] > 1 and t.stride(0) != stride:
         _arg_error(f"{name} token stride {t.stride(0)} differs from the shape's {stride}")
     if t.stride(-1) != 1 or (t.dim() == 3 and t.shape[1] > 1 and t.stride(1) != t.shape[2]):
@@ -370,6 +376,30 @@ def cp_ulysses_share(shape, S, sp, sp_rank, q, k, v, doc, o, lse, dout=None, dq=
     _check(lib.cp_ulysses_share(ctypes.byref(shape), S, sp, sp_rank, _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(doc), _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                 _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20       # CP_NOALLOC_SCRATCH_BYTES
+
+
+def cp_ulysses_share_noalloc(shape, S, sp, sp_rank, q, k, v, doc, o, lse, dout=None, dq=None, dk=None, dv=None,
+                             stream=None):
+    """cp_ulysses_share without a workspace: Delta lives in the library's
+    built-in per-GPU scratch (NOALLOC_SCRATCH_BYTES); calls that overlap on
+    one GPU race."""
+    lib = load()
+    hq, hkv = shape.hq // sp, shape.hkv // sp
+    _tokens("q", q, shape.q_stride)
+    _tokens("k", k, shape.kv_stride)
+    _tokens("v", v, shape.kv_stride)
+    _dense("o", o, (S, hq, shape.d))
+    _dense("lse", lse, (hq, S))
+    _dense("dout", dout, (S, hq, shape.d))
+    _dense("dq", dq, (S, hq, shape.d))
+    _dense("dk", dk, (S, hkv, shape.d))
+    _dense("dv", dv, (S, hkv, shape.d))
+    _check(lib.cp_ulysses_share_noalloc(ctypes.byref(shape), S, sp, sp_rank, _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(doc), _ptr(o), _dtype_code(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), _stream(stream)))
 
 
 def cp_allgather_workspace_bytes(shape, S, P, has_doc, backward):

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -721,10 +722,14 @@ size_t cp_ulysses_workspace_bytes(const cp_shape* sh, int64_t S, int32_t sp, int
   return backward ? align256((size_t)(sh->hq / sp) * S * 4) : 0;
 }
 
-cp_status cp_ulysses_share(const cp_shape* sh_full, int64_t S, int32_t sp, int32_t sp_rank, const void* q,
-                           const void* k, const void* v, const int32_t* doc, void* o, cp_dtype o_dtype, float* lse,
-                           const void* dout, float* dq, float* dk, float* dv, void* workspace, size_t ws_bytes,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Arguments of a Ulysses share, apart from its scratch.
+cp_status ulysses_args(const cp_shape* sh_full, int64_t S, int32_t sp, int32_t sp_rank, const void* q,
+                       const void* k, const void* v, void* o, cp_dtype o_dtype, float* lse, const void* dout,
+                       float* dq, float* dk, float* dv) {
   CP_TRY(check_shape(sh_full));
   if (S <= 0) return fail(CP_ERR_ARG, "S=%lld out of range", (long long)S);
   if (S > kMaxTokens) return fail(CP_ERR_UNSUPPORTED, "S=%lld above %d tokens", (long long)S, kMaxTokens);
@@ -744,10 +749,16 @@ cp_status cp_ulysses_share(const cp_shape* sh_full, int64_t S, int32_t sp, int32
     CP_TRY(check_ptr(dq, "dq"));
     CP_TRY(check_ptr(dk, "dk"));
     CP_TRY(check_ptr(dv, "dv"));
-    const size_t need = cp_ulysses_workspace_bytes(sh_full, S, sp, 1);
-    if (!workspace || ws_bytes < need) return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes required", need);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(CP_ERR_ALIGN, "workspace must be 256-byte aligned");
   }
+  return CP_OK;
+}
+
+// The share's kernels on `st`; dlt: scratch of (hq/sp)*S fp32 for Delta
+// (backward only).
+cp_status ulysses_drive(const cp_shape* sh_full, int64_t S, int32_t sp, int32_t sp_rank, const void* q,
+                        const void* k, const void* v, const int32_t* doc, void* o, cp_dtype o_dtype, float* lse,
+                        const void* dout, float* dq, float* dk, float* dv, float* dlt, hipStream_t st) {
+  const bool backward = dout != nullptr;
   cp_shape sh = *sh_full;
   sh.hq = sh_full->hq / sp;
   sh.hkv = sh_full->hkv / sp;
@@ -757,11 +768,9 @@ cp_status cp_ulysses_share(const cp_shape* sh_full, int64_t S, int32_t sp, int32
   const char* vs_ptr = (const char*)v + (size_t)sp_rank * sh.hkv * sh.d * esz;
   if (!aligned16(qs_ptr) || !aligned16(ks_ptr)) return fail(CP_ERR_ALIGN, "head slice not 16-byte aligned");
   const cp_span span = run_span(0, (int32_t)S, S, 0, doc);
-  hipStream_t st = (hipStream_t)stream;
   CP_TRY(check_seq_ids(sh_full, doc, S, st));
   CP_TRY_HIP(run_fwd(&sh, qs_ptr, span, ks_ptr, vs_ptr, span, o, o_dtype, lse, S, st), "ulysses forward");
   if (backward) {
-    float* dlt = (float*)workspace;
     // one chunk holds every pair: the gradients are written, not added to
     // (run_bwd zero-fills first where the kernels only accumulate)
     CP_TRY_HIP(launch_delta(S, sh.hq, sh.d, o, o_dtype == CP_F32, dout, sh.dtype == CP_F32, dlt, S, st),
@@ -770,6 +779,78 @@ cp_status cp_ulysses_share(const cp_shape* sh_full, int64_t S, int32_t sp, int32
                "ulysses backward");
   }
   return ok();
+}
+
+}  // namespace
+
+// Scratch of cp_ulysses_share_noalloc: the backward's Delta rows live in a
+// file-scope device array instead of a caller workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` only names the symbol; its device address on the current GPU is
+// looked up once per device (hipGetSymbolAddress) and only that address is
+// handed to kernels.
+constexpr size_t kNoallocScratchBytes = CP_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, resolved on the first
+// call per device and kept.
+cp_status scratch_address(void** out) {
+  int dev = -1;
+  CP_TRY_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CP_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    CP_TRY_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch address");
+    if (!p) return fail(CP_ERR_HIP, "scratch address: null");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status cp_ulysses_share(const cp_shape* sh_full, int64_t S, int32_t sp, int32_t sp_rank, const void* q,
+                           const void* k, const void* v, const int32_t* doc, void* o, cp_dtype o_dtype, float* lse,
+                           const void* dout, float* dq, float* dk, float* dv, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  CP_TRY(ulysses_args(sh_full, S, sp, sp_rank, q, k, v, o, o_dtype, lse, dout, dq, dk, dv));
+  if (dout) {
+    const size_t need = cp_ulysses_workspace_bytes(sh_full, S, sp, 1);
+    if (!workspace || ws_bytes < need) return fail(CP_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(CP_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  return ulysses_drive(sh_full, S, sp, sp_rank, q, k, v, doc, o, o_dtype, lse, dout, dq, dk, dv, (float*)workspace,
+                       (hipStream_t)stream);
+}
+
+cp_status cp_ulysses_share_noalloc(const cp_shape* sh_full, int64_t S, int32_t sp, int32_t sp_rank, const void* q,
+                                   const void* k, const void* v, const int32_t* doc, void* o, cp_dtype o_dtype,
+                                   float* lse, const void* dout, float* dq, float* dk, float* dv, void* stream) {
+  CP_TRY(ulysses_args(sh_full, S, sp, sp_rank, q, k, v, o, o_dtype, lse, dout, dq, dk, dv));
+  if (sh_full->flags & CP_CHECK_DOCS)
+    return fail(CP_ERR_ARG, "CP_CHECK_DOCS copies ids to the host and waits; check them with cp_check_docs first");
+  float* dlt = nullptr;
+  if (dout) {
+    const size_t need = cp_ulysses_workspace_bytes(sh_full, S, sp, 1);
+    if (need > kNoallocScratchBytes)
+      return fail(CP_ERR_WORKSPACE, "Delta needs %zu bytes, above the %zu-byte built-in scratch", need,
+                  kNoallocScratchBytes);
+    void* p = nullptr;
+    CP_TRY(scratch_address(&p));
+    dlt = (float*)p;
+  }
+  return ulysses_drive(sh_full, S, sp, sp_rank, q, k, v, doc, o, o_dtype, lse, dout, dq, dk, dv, dlt,
+                       (hipStream_t)stream);
 }
 
 static cp_status check_a2a(int64_t S, int32_t h, int32_t d, int32_t elt_bytes, int32_t sp, int32_t rank,

@@ -249,3 +249,22 @@ def test_ring_layout_table_checks(lib, chunks, status):
     st = lib.cp_ring_emulate_layout(ctypes.byref(sh), 1024, 4, 0, None, P, P, P, None, P, cp.CP_BF16, P,
                                     None, None, None, None, None, 0, None)
     assert st == cp.CP_ERR_ARG
+
+
+def test_ulysses_noalloc_refusals_before_launch(lib):
+    """The no-allocation Ulysses share refuses, before touching the GPU, a
+    backward whose Delta rows exceed the built-in scratch and the checked
+    document mode (which would copy to the host and wait)."""
+    sh = _shape()
+    P = ctypes.c_void_p(0x10000)
+    big = cp.NOALLOC_SCRATCH_BYTES // (4 * sh.hq) + 64
+    st = lib.cp_ulysses_share_noalloc(ctypes.byref(sh), big, 1, 0, P, P, P, None, P, cp.CP_BF16, P,
+                                      P, P, P, P, None)
+    assert st == cp.CP_ERR_WORKSPACE, lib.cp_last_error().decode()
+    shc = _shape(flags=cp.CP_CHECK_DOCS)
+    st = lib.cp_ulysses_share_noalloc(ctypes.byref(shc), 1024, 1, 0, P, P, P, None, P, cp.CP_BF16, P,
+                                      P, P, P, P, None)
+    assert st == cp.CP_ERR_ARG
+    st = lib.cp_ulysses_share_noalloc(ctypes.byref(sh), 1024, 4, 0, P, P, P, None, P, cp.CP_BF16, P,
+                                      P, P, P, P, None)
+    assert st == cp.CP_ERR_ARG                                   # sp=4 does not divide hkv=2
