@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-workloads", action="store_true",
                     help="with the default workload, skip the short runs of the other workloads")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="only measure the vendor library's bf16 GEMM throughput (16384^3) and print it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (3 times), the reference for "
                          "scaling HBM traffic counters")
@@ -420,6 +422,23 @@ def allgather_share(wl, cp, torch, steps, ms_ring):
             "vs_ring_step": round(ms / ms_ring, 4)}
 
 
+def gemm_ceiling(torch, n=16384, iters=10):
+    """The MFMA throughput the vendor library reaches on this GPU: one large
+    square bf16 GEMM (torch.matmul, i.e. hipBLASLt), timed with events.  Not
+    part of the attention path; reported beside the roofline as the practical
+    ceiling under sustained load, where the shader clock drops well below the
+    2.4 GHz that the published 2.5 PFLOP/s assumes."""
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    per = timed_steps(lambda: a @ b, torch, 3, iters)
+    ms = float(np.median(per))
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"what": f"bf16 GEMM {n}x{n}x{n} via torch.matmul (hipBLASLt)", "ms_median": round(ms, 4),
+            "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def timed_steps(fn, torch, warmup, steps):
     """Per-step milliseconds of `steps` calls after `warmup`, each bracketed by
     events on the current stream."""
@@ -534,6 +553,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}), flush=True)
         return
+    if args.gemm_ceiling:
+        print(json.dumps({"measured_gemm_ceiling": gemm_ceiling(torch)}), flush=True)
+        return
     wl = Workload(args.workload, torch, cp, cpinputs)
     torch.cuda.synchronize()
     print(f"[bench] workload {args.workload} ready", file=sys.stderr, flush=True)
@@ -598,12 +620,15 @@ def main():
         dom = max((n for n in kt if "flops" in kt[n]), key=lambda n: kt[n]["ms"])
         ach = kt[dom]["flops"] / (kt[dom]["ms"] * 1e-3) / 1e12
         traffic = measured_traffic(dom, args.workload)
+        ceiling = gemm_ceiling(torch)
         out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                            "traffic": None if traffic is None else round(traffic),
                            "flops_per_launch": kt[dom]["flops"], "ms_per_launch": round(kt[dom]["ms"], 4),
-                           "source_sha256_16": kernel_source_hash(dom)}
+                           "source_sha256_16": kernel_source_hash(dom),
+                           "frac_of_measured_gemm": round(ach / ceiling["tflops"], 4),
+                           "measured_gemm_ceiling": ceiling}
     if wl.name == "docs_128k":
         # rank balance of a ring over these documents (host integer work): the
         # zigzag layout vs the document-aware two-chunk pairing

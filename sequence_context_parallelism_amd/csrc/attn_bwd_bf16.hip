@@ -292,21 +292,50 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
   // wave that loaded the LSE (Delta) row converts it in LDS once its loads
   // have landed (prepare): nl = -LSE log2 e, and -Delta.
   const TileLoader<D, BQ, KNW> ldq(a.q_stride * 2, wave, lane), ldo((int64_t)a.hq * D * 2, wave, lane);
-  auto issue = [&](int it, uint32_t Qd, uint32_t Od, uint32_t Ld, uint32_t Dd, uint32_t Xd) {
-    const int32_t qt = qt1 - 1 - it / G;
-    const int head = kvh * G + it % G;
-    if (qt * BQ + BQ <= Lq) {   // whole tile: precomputed lane offsets
-      ldq.load(Qd, (const char*)(a.q + (int64_t)qt * BQ * a.q_stride + (int64_t)head * D));
-      ldo.load(Od, (const char*)(a.dout + ((int64_t)qt * BQ * a.hq + head) * D));
-    } else {                    // ragged last tile: rows clamped
-      tile_load_lds<D, BQ, KNW>(Qd, a.q + (int64_t)head * D, a.q_stride, qt * BQ, Lq, wave, lane);
-      tile_load_lds<D, BQ, KNW>(Od, a.dout + (int64_t)head * D, (int64_t)a.hq * D, qt * BQ, Lq, wave, lane);
+  // The next item to issue, kept as running byte pointers (wave-uniform, in
+  // SGPRs) that move by constant steps: one head on, or back to the group's
+  // first head and one query tile down.  No division or 64-bit multiply per
+  // item.
+  struct Cursor {
+    int32_t qt, g;
+    const char *q, *o;
+    const float *l, *d;
+  };
+  Cursor nx{qt1 - 1, 0,
+            (const char*)(a.q + (int64_t)(qt1 - 1) * BQ * a.q_stride + (int64_t)kvh * G * D),
+            (const char*)(a.dout + ((int64_t)(qt1 - 1) * BQ * a.hq + (int64_t)kvh * G) * D),
+            a.lse + (int64_t)kvh * G * a.lse_ld, a.delta + (int64_t)kvh * G * a.lse_ld};
+  const int64_t q_back = (int64_t)BQ * a.q_stride * 2 + (int64_t)G * D * 2;    // bytes
+  const int64_t o_back = ((int64_t)BQ * a.hq + G) * D * 2;
+  const int64_t l_back = (int64_t)G * a.lse_ld;                                // floats
+  auto advance = [&](Cursor& c) {
+    c.q += D * 2;
+    c.o += D * 2;
+    c.l += a.lse_ld;
+    c.d += a.lse_ld;
+    if (++c.g == G) {
+      c.g = 0;
+      --c.qt;
+      c.q -= q_back;
+      c.o -= o_back;
+      c.l -= l_back;
+      c.d -= l_back;
     }
-    const int32_t row = min(qt * BQ + lane, Lq - 1);
+  };
+  auto issue = [&](const Cursor& c, uint32_t Qd, uint32_t Od, uint32_t Ld, uint32_t Dd, uint32_t Xd) {
+    if (c.qt * BQ + BQ <= Lq) {   // whole tile: precomputed lane offsets
+      ldq.load(Qd, c.q);
+      ldo.load(Od, c.o);
+    } else {                      // ragged last tile: rows clamped
+      const int head = kvh * G + c.g;
+      tile_load_lds<D, BQ, KNW>(Qd, a.q + (int64_t)head * D, a.q_stride, c.qt * BQ, Lq, wave, lane);
+      tile_load_lds<D, BQ, KNW>(Od, a.dout + (int64_t)head * D, (int64_t)a.hq * D, c.qt * BQ, Lq, wave, lane);
+    }
+    const int32_t row = min(c.qt * BQ + lane, Lq - 1);
     if (wave == 0)
-      row_load_lds(a.lse + (int64_t)head * a.lse_ld, row, Ld);
+      row_load_lds(c.l, row, Ld);
     else if (wave == 1)
-      row_load_lds(a.delta + (int64_t)head * a.lse_ld, row, Dd);
+      row_load_lds(c.d, row, Dd);
     else if (wave == 2 && docs)
       row_load_lds(qs.doc, row, Xd);
   };
@@ -324,7 +353,8 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
       tile_load_lds<D, BKG, KNW>(S0 + VT, a.v + (int64_t)kvh * D, a.kv_stride, k0, Lk, wave, lane);
       tile_load_lds<D, BKG, KNW>(S0 + VT + KV_GAP<D>, a.k + (int64_t)kvh * D, a.kv_stride, k0, Lk, wave, lane);
     }
-    issue(0, S0 + Q0, S0 + O0, S0 + L0, S0 + N0, S0 + X0);
+    issue(nx, S0 + Q0, S0 + O0, S0 + L0, S0 + N0, S0 + X0);
+    advance(nx);
   }
   const uint32_t Vw = S0 + VT + kb * (BKW * D * 2);   // this wave's 32 V rows
 
@@ -359,10 +389,15 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
   if (nitems > 0) prepare(S0 + L0, S0 + N0);
   __syncthreads();
 
+  int32_t cur_qt = qt1 - 1, cur_g = 0;   // the item being computed
   auto step = [&](int it, uint32_t Qc, uint32_t Oc, uint32_t Lc, uint32_t Dc, uint32_t Xc, uint32_t Qn,
                   uint32_t On, uint32_t Ln, uint32_t Dn, uint32_t Xn) {
-    if (it + 1 < nitems) issue(it + 1, Qn, On, Ln, Dn, Xn);
-    const int32_t qa0 = (qt1 - 1 - it / G) * BQ;
+    if (it + 1 < nitems) {
+      issue(nx, Qn, On, Ln, Dn, Xn);
+      advance(nx);
+    }
+    const int32_t qa0 = cur_qt * BQ;
+    if (++cur_g == G) { cur_g = 0; --cur_qt; }
     const int32_t wq0 = qa0 + 32 * qh, wq1 = min(Lq, wq0 + 32);   // this wave's query rows
     bool live = wave_has_keys && wq0 < Lq && wq1 - 1 >= q_none;
     bool full = wq1 - wq0 == 32 && wq0 >= q_all && wk1 - wk0 == BKW;
