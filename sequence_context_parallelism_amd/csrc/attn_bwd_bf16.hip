@@ -10,18 +10,20 @@
 //
 // Two kernels, neither with atomics (deterministic):
 //   dkdv (KV-outer): a work-group of 8 waves (two per SIMD) owns 128 keys of
-//     one KV head and streams 64-row tiles of Q and dO for every query head
-//     of the GQA group through LDS (direct-to-LDS loads, double-buffered).
-//     The work-group's K and V rows stay resident in LDS.  Wave w takes keys
-//     32(w % 4) .. +31 (their dK^T, dV^T accumulators in VGPRs) against query
-//     rows 32(w / 4) .. +31 of each tile.  Per tile: S = Q K^T,
-//     dP = dO V^T - Delta (row reads of both operands; the dP accumulator
-//     starts at -Delta), P = exp2(S c + nl) with nl = -LSE log2 e, dS = P dP,
-//     then dV^T += dO^T P and dK^T += Q^T dS (A operands read with the LDS
-//     transpose read; P and dS go from the accumulator layout straight into
-//     the B operand).  4 MFMA products per (query, key) pair.  The two waves
-//     of a key block sum their partial dK, dV through LDS at the end; the
-//     softmax scale of dK is applied once, there.
+//     one KV head and streams 64-row items (query tile, query head) of Q, dO
+//     and the row arrays through LDS (direct-to-LDS loads, three buffers).
+//     The two waves of a SIMD own the same 32 keys and split the products:
+//     one holds the K rows in VGPRs and computes S = Q K^T,
+//     P = exp2(S c + nl) (nl = -LSE log2 e) and dV^T += dO^T P; the other
+//     holds the V rows and computes dP = dO V^T - Delta (accumulator started
+//     at -Delta), dS = P dP with P passed through LDS, and dK^T += Q^T dS.
+//     4 MFMA products per (query, key) pair, each wave reading one operand
+//     per MFMA from LDS (row reads, or the LDS transpose read for the
+//     gradient products' A operands).  The softmax scale of dK is applied
+//     once, at the end.  Key tiles kt and nkt-1-kt run as partners on one
+//     XCD, the first walking its query tiles from the last, the second from
+//     the first (dkdv_work in common.h), so that the work-groups of an XCD
+//     share the Q/dO tiles they copy through its L2.
 //   dq (Q-outer): a work-group of 8 waves (two per SIMD) owns 64 query rows
 //     of 4 query heads sharing a KV head, 32 rows of one head per wave (like
 //     the forward), and streams 64-key tiles of K and V.  Per tile:
@@ -30,9 +32,9 @@
 // With two waves per SIMD each wave's exp/dS VALU work runs beside the other
 // wave's MFMAs.  Masked entries get S = -inf before the exponential, so P = 0;
 // fully masked tiles are skipped and element masks run only on partial or
-// ragged tiles.  Heavy-first orders: ascending keys for dkdv, descending
-// queries for dq.  Inside a dkdv work-group the query tiles run from the last
-// one down.
+// ragged tiles.  The dq work-groups run heavy-first (descending queries).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "tile_io.h"
@@ -61,165 +63,24 @@ __device__ inline void lds_stf(uint32_t a, float x) { *(__attribute__((address_s
 __device__ inline float neg_lse2(float lse) { return lse == -INFINITY ? -INFINITY : -lse * LOG2E; }
 
 // ============================== dK, dV ======================================
-
-// K rows sit this many bytes after the V rows in LDS (one 128-key tile)
-template <int D>
-constexpr uint32_t KV_GAP = 128 * D * 2;
-
-template <int D>
-struct KvState {
-  f32x16 dka[D / 32], dva[D / 32]; // dK^T (unscaled), dV^T accumulators [d block]
-  int32_t qlim;                    // queries [qlim, ..) see this lane's key causally
-  int32_t kdoc;
-  bool kvalid;
-};
-
-// Element mask of block qb: S = -inf where the lane's key is not visible.
-template <int D>
-__device__ inline void dkdv_mask(const KvState<D>& st, f32x16& s, uint32_t QDt, int32_t qa0, int qb,
-                                 int32_t Lq, bool docs, int hh) {
-  asm volatile("; partial tile" ::: "memory");   // keeps the caller's branch real (no if-conversion)
-  int qbase = qb * 32 + hh * 4;
-  asm volatile("" : "+v"(qbase));   // recomputed here, not hoisted out of the tile loop
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int qr = qbase + (r >> 2) * 8 + (r & 3);
-    const int32_t qidx = qa0 + qr;
-    const bool ok = st.kvalid & (qidx < Lq) & (qidx >= st.qlim) & (!docs | (lds_ld4i(QDt + 4 * qr) == st.kdoc));
-    s[r] = ok ? s[r] : -INFINITY;
-  }
-}
-
-// The wave's 32 keys against the 32-query block qb of the tile (rows
-// 32 qb .. 32 qb + 31): S and dP - Delta (accumulator element r: key = the
-// lane's key, query row qb*32 + 8(r/4) + 4hh + r%4; the dP accumulator starts
-// at -Delta), P = exp2(S c + nl), dS = P dP, then dV^T += dO^T P and
-// dK^T += Q^T dS over that block's two 16-query slots.  rq and tq carry the
-// block's row offset in their lane bases; vb is the lane's address in the
-// wave's V rows (its K rows KV_GAP bytes on), so the tile offsets and the
-// per-step offsets fold into the LDS instructions' immediates.
 //
-// Explicit software pipeline (scheduling walls keep the order): operand
-// reads run two MFMAs ahead through a two-entry register ring, and slot 1's
-// P/dS VALU work is spread over slot 0's gradient MFMAs.  The wave raises its
-// issue priority for its two MFMA stretches and drops it for the mask and
-// slot 0's P/dS, so the SIMD's other wave, if it is in a VALU stretch, yields
-// the issue slots to the MFMAs, and its own VALU work fills the gaps.
-template <int D>
-__device__ inline void dkdv_block(KvState<D>& st, const RowReader<D>& rq, const TrReader<D>& tq, uint32_t Qt,
-                                  uint32_t Ot, uint32_t vb, uint32_t Nl, uint32_t NDt, uint32_t QDt, int32_t qa0,
-                                  int qb, int32_t Lq, bool mask, bool docs, float c, int lane) {
-  constexpr int NKD = D / 16, NDB = D / 32;
-  const int hh = lane >> 5;
-  f32x16 s, dp;
-  {
-    f32x16 init;   // -Delta of the element's query row
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 d4 = lds_f4(NDt + 4 * (qb * 32 + j * 8 + hh * 4));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) init[j * 4 + i] = d4[i];
-    }
-    bf16x8 ra[2], ro[2], rv[2], rk[2];
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      ra[k] = rq.at(Qt, 0, k);
-      ro[k] = rq.at(Ot, 0, k);
-      rv[k] = lds_ld16(vb ^ (uint32_t)(k << 5));
-      rk[k] = lds_ld16((vb ^ (uint32_t)(k << 5)) + KV_GAP<D>);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kd = 0; kd < NKD; ++kd) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[kd & 1], rk[kd & 1], kd ? s : f32x16{}, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ro[kd & 1], rv[kd & 1], kd ? dp : init, 0, 0, 0);
-      if (kd + 2 < NKD) {
-        ra[kd & 1] = rq.at(Qt, 0, kd + 2);
-        ro[kd & 1] = rq.at(Ot, 0, kd + 2);
-        rv[kd & 1] = lds_ld16(vb ^ (uint32_t)((kd + 2) << 5));
-        rk[kd & 1] = lds_ld16((vb ^ (uint32_t)((kd + 2) << 5)) + KV_GAP<D>);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  __builtin_amdgcn_s_setprio(0);
-  if (mask) dkdv_mask<D>(st, s, QDt, qa0, qb, Lq, docs, hh);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // gradient operands of MFMA pair m (slot m / NDB, d block m % NDB)
-  bf16x8 go[2], gq[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    go[m] = tq.at(Ot, 16 * (m / NDB), m % NDB);
-    gq[m] = tq.at(Qt, 16 * (m / NDB), m % NDB);
-  }
-  bf16x8 pf[2], dsf[2];
-  auto pds = [&](int r, const f32x4& n4) {
-    const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, n4[r & 3]));
-    pf[r >> 3][r & 7] = (__bf16)p;
-    dsf[r >> 3][r & 7] = (__bf16)(p * dp[r]);
-  };
-  {
-    const f32x4 n0 = lds_f4(Nl + 4 * (qb * 32 + 0 * 8 + hh * 4));
-    const f32x4 n1 = lds_f4(Nl + 4 * (qb * 32 + 1 * 8 + hh * 4));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pds(r, n0);
-#pragma unroll
-    for (int r = 4; r < 8; ++r) pds(r, n1);
-  }
-  const f32x4 n2 = lds_f4(Nl + 4 * (qb * 32 + 2 * 8 + hh * 4));
-  const f32x4 n3 = lds_f4(Nl + 4 * (qb * 32 + 3 * 8 + hh * 4));
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(1);
-  constexpr int PER = 8 / NDB;   // slot-1 elements per slot-0 MFMA pair
-#pragma unroll
-  for (int m = 0; m < 2 * NDB; ++m) {
-    const int u = m / NDB, db = m % NDB;
-    st.dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(go[m & 1], pf[u], st.dva[db], 0, 0, 0);
-    st.dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gq[m & 1], dsf[u], st.dka[db], 0, 0, 0);
-    if (m + 2 < 2 * NDB) {
-      go[m & 1] = tq.at(Ot, 16 * ((m + 2) / NDB), (m + 2) % NDB);
-      gq[m & 1] = tq.at(Qt, 16 * ((m + 2) / NDB), (m + 2) % NDB);
-    }
-    if (m < NDB) {
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const int r = 8 + m * PER + e;
-        pds(r, r < 12 ? n2 : n3);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  __builtin_amdgcn_s_setprio(0);
-}
-
-__device__ inline void lds_st4(uint32_t a, const f32x4& x) {
-  *(__attribute__((address_space(3))) f32x4*)(uintptr_t)a = x;
-}
-
-// Park a 32-key x D accumulator set (accumulator layout) at LDS address P, or
-// add the parked one into it: lane-contiguous 16-byte groups.
-template <int D>
-__device__ inline void park_acc(uint32_t P, const f32x16 (&acc)[D / 32], int lane) {
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      lds_st4(P + ((db * 4 + j) * 64 + lane) * 16,
-              f32x4{acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]});
-}
-template <int D>
-__device__ inline void unpark_add(uint32_t P, f32x16 (&acc)[D / 32], int lane) {
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 x = lds_f4(P + ((db * 4 + j) * 64 + lane) * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[db][4 * j + i] += x[i];
-    }
-}
+// The work-group owns 128 keys of one KV head and streams 64-row items
+// (query tile, query head) through LDS, triple-buffered.  Each SIMD holds 32
+// of the keys and its two waves split the four products of the item's two
+// 32-row blocks between them:
+//   wave "P" (waves 0-3): S = Q K^T with the wave's K rows in VGPRs,
+//     P = exp2(S c + nl), dV^T += dO^T P;  P goes to its partner through LDS;
+//   wave "dS" (waves 4-7): dP = dO V^T - Delta with the wave's V rows in
+//     VGPRs, dS = P dP, dK^T += Q^T dS.
+// Each wave reads one 1 KiB operand from LDS per MFMA (the other is in
+// registers) and keeps one set of accumulators (dV^T or dK^T) for all rows,
+// so the end needs no exchange between waves.  Interval k (between two
+// work-group barriers) runs item k's score products and item k-1's gradient
+// products: P and dP of item k-1 are carried in registers across one
+// barrier, the Q/dO tiles of items k-1 and k are resident while item k+1's
+// copy lands.  Both 32-row blocks of an item are always computed (their two
+// accumulator chains interleave); a block with no allowed entry gets P = 0
+// from the element mask, and an item with none is skipped whole.
 
 // dst[key row, d] += mul * acc, or = with `store` (accumulator layout:
 // d = db*32 + 8j + 4hh + i)
@@ -237,42 +98,177 @@ __device__ inline void add_rows(float* dst, const f32x16 (&acc)[D / 32], float m
     }
 }
 
-constexpr int KNW = 8;   // waves per dkdv work-group: 4 key blocks x 2 query halves
+constexpr int KNW = 8;   // waves per dkdv work-group: 4 key blocks x 2 roles
+
+template <int D>
+struct KvState {
+  bf16x8 kv[D / 16];   // this wave's K (P wave) or V (dS wave) rows: MFMA B operands, lane = key
+  f32x16 acc[D / 32];  // dV^T (P wave) or dK^T (dS wave, unscaled)
+  f32x16 sc[2];        // P wave: S of the item's two blocks; dS wave: dP - Delta
+  bf16x8 pb[2][2];     // P wave: P of the two blocks (B operand layout), kept for the gradient
+  int32_t qlim, kdoc;
+  bool kvalid;
+};
+
+// Scores of both 32-row blocks of the item in tile Tt, their accumulator
+// chains interleaved: S (P wave: A = Q rows) or dP (dS wave: A = dO rows,
+// accumulators from -Delta at NDt).
+template <int D, bool DS>
+__device__ inline void kv_scores(KvState<D>& st, const RowReader<D>& rq, uint32_t Tt, uint32_t NDt, int hh) {
+  constexpr int NKD = D / 16;
+  if constexpr (DS) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 d4 = lds_f4(NDt + 4 * (qb * 32 + j * 8 + hh * 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.sc[qb][j * 4 + i] = d4[i];
+      }
+  }
+  bf16x8 r0[2], r1[2];
+  r0[0] = rq.at(Tt, 0, 0);
+  r1[0] = rq.at(Tt, 1, 0);
+  r0[1] = rq.at(Tt, 0, 1);
+  r1[1] = rq.at(Tt, 1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kd = 0; kd < NKD; ++kd) {
+    st.sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r0[kd & 1], st.kv[kd], (DS || kd) ? st.sc[0] : f32x16{}, 0, 0, 0);
+    st.sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r1[kd & 1], st.kv[kd], (DS || kd) ? st.sc[1] : f32x16{}, 0, 0, 0);
+    if (kd + 2 < NKD) {
+      r0[kd & 1] = rq.at(Tt, 0, kd + 2);
+      r1[kd & 1] = rq.at(Tt, 1, kd + 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Element mask of block qb: S = -inf where the lane's key is not visible.
+template <int D>
+__device__ inline void kv_mask(const KvState<D>& st, f32x16& s, uint32_t QDt, int32_t qa0, int qb, int32_t Lq,
+                               bool docs, int hh) {
+  asm volatile("; partial tile" ::: "memory");   // keeps the caller's branch real (no if-conversion)
+  int qbase = qb * 32 + hh * 4;
+  asm volatile("" : "+v"(qbase));
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int qr = qbase + (r >> 2) * 8 + (r & 3);
+    const int32_t qidx = qa0 + qr;
+    const bool ok = st.kvalid & (qidx < Lq) & (qidx >= st.qlim) & (!docs | (lds_ld4i(QDt + 4 * qr) == st.kdoc));
+    s[r] = ok ? s[r] : -INFINITY;
+  }
+}
+
+// P wave: P = exp2(S c + nl) of both blocks into st.pb and the exchange area.
+template <int D>
+__device__ inline void kv_p(KvState<D>& st, uint32_t Nl, float c, int hh, uint32_t Xc) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 n4 = lds_f4(Nl + 4 * (qb * 32 + j * 8 + hh * 4));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = j * 4 + i;
+        st.pb[qb][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(st.sc[qb][r], c, n4[i]));
+      }
+    }
+    *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(Xc + qb * 2048u) = st.pb[qb][0];
+    *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(Xc + qb * 2048u + 1024u) = st.pb[qb][1];
+  }
+}
+
+// Gradient products of both blocks of the item in tile At: dV^T += dO^T P
+// (P wave, g = st.pb) or dK^T += Q^T dS (dS wave, dS formed here from the
+// partner's P at Xp and st.sc; block 1's dS is formed between block 0's MFMAs).
+template <int D, bool DS>
+__device__ inline void kv_grad(KvState<D>& st, const TrReader<D>& tq, uint32_t At, uint32_t Xp) {
+  constexpr int NDB = D / 32, NM = 2 * NDB, PER = 16 / NM;
+  bf16x8 g0[2], g1[2], p1[2];
+  if constexpr (DS) {
+    bf16x8 p0[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      p0[h] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(Xp + h * 1024u);
+      p1[h] = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(Xp + 2048u + h * 1024u);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) g0[r >> 3][r & 7] = (__bf16)((float)p0[r >> 3][r & 7] * st.sc[0][r]);
+  } else {
+    g0[0] = st.pb[0][0];
+    g0[1] = st.pb[0][1];
+    g1[0] = st.pb[1][0];
+    g1[1] = st.pb[1][1];
+  }
+  bf16x8 ga[2];
+  ga[0] = tq.at(At, 0, 0);
+  ga[1] = tq.at(At, 16 * (1 / NDB), 1 % NDB);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int m = 0; m < 2 * NM; ++m) {
+    const int qb = m / NM, mm = m % NM, u = mm / NDB, db = mm % NDB;
+    st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[m & 1], qb ? g1[u] : g0[u], st.acc[db], 0, 0, 0);
+    if (m + 2 < 2 * NM) {
+      const int n = m + 2, nqb = n / NM, nm = n % NM;
+      ga[m & 1] = tq.at(At, 32 * nqb + 16 * (nm / NDB), nm % NDB);
+    }
+    if constexpr (DS) {
+      if (m < NM) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const int r = m * PER + e;
+          g1[r >> 3][r & 7] = (__bf16)((float)p1[r >> 3][r & 7] * st.sc[1][r]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+constexpr int SNB = 3;   // Q/dO tile buffers (dkdv)
 
 template <int D>
 __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
-  // LDS arena: Q and dO tiles (double-buffered), then per-row LSE (as
-  // -LSE log2 e), -Delta and doc ids, each double-buffered, then the work-
-  // group's V rows and K rows (read as MFMA B operands).  After the tile loop
-  // the tile area holds the parked partial accumulators (4 x 32 keys x D
-  // floats = as many bytes as the four tiles).
+  // LDS arena: SNB Q tiles, SNB dO tiles, then SNB sets of per-row arrays
+  // (-LSE log2 e, -Delta, doc ids), then the P exchange area: [SNB buffers]
+  // [4 SIMD pairs][2 blocks][2 halves] x 64 lanes x 16 bytes.  Item k uses
+  // set k % SNB of each, so a loop unrolled SNB times addresses them all
+  // with constant offsets.
   constexpr uint32_t TB = BQ * D * 2, RW = BQ * 4;
-  constexpr uint32_t Q0 = 0, Q1 = TB, O0 = 2 * TB, O1 = 3 * TB;
-  constexpr uint32_t L0 = 4 * TB, L1 = L0 + RW, N0 = L1 + RW, N1 = N0 + RW, X0 = N1 + RW, X1 = X0 + RW;
-  constexpr uint32_t VT = X1 + RW;   // V rows, then K rows KV_GAP bytes on
-  static_assert(4 * BKW * D * 4 <= 4 * TB, "parked accumulators must fit in the tile area");
-  static_assert(VT % 16 == 0, "V tile alignment");
-  static_assert(KV_GAP<D> == BKG * D * 2, "K rows follow the V rows");
-  __shared__ __attribute__((aligned(16))) char smem[VT + 2 * BKG * D * 2];
+  constexpr uint32_t QB0 = 0, OB0 = SNB * TB, RB0 = 2 * SNB * TB;
+  constexpr uint32_t XB0 = RB0 + SNB * 3 * RW;
+  constexpr uint32_t XSZ = SNB * 4 * 2 * 2 * 1024;
+  static_assert(XB0 % 16 == 0, "exchange alignment");
+  __shared__ __attribute__((aligned(16))) char smem[XB0 + XSZ];
   const uint32_t S0 = lds_addr(smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
-  const int kb = wave & 3, qh = wave >> 2;                      // key block, query half
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = wave & 3;                 // 32-key block of the work-group's 128
+  const bool is_ds = (wave >> 2) != 0;     // wave-uniform role
   const int lq = lane & 31, hh = lane >> 5;
 
-  int32_t kvh, kt;                                      // ascending kt = heavy first
-  if (!xcd_work(blockIdx.x, a.hkv, a.nkt, kvh, kt)) return;
+  // one key tile of one KV head; dir: the order of its query tiles
+  int32_t kvh, kt, dir;
+  if (!dkdv_work(blockIdx.x, a.hkv, a.nkt, kvh, kt, dir)) return;
 
   const SpanD qs = a.qs, ks = a.ks;
   const int32_t Lq = span_len(qs), Lk = span_len(ks);
   const bool causal = a.causal != 0;
   const bool docs = qs.doc != nullptr;
+  const int G = a.G;
+  const TileLoader<D, BQ, KNW> ldq(a.q_stride * 2, wave, lane), ldo((int64_t)a.hq * D * 2, wave, lane);
+  const float c = a.scale * LOG2E;
+  const RowReader<D> rq(lane);
+  const TrReader<D> tq(lane);
+  // this lane's 16-byte slot in the exchange area of pair kb: + buf * 16384 + qb * 2048 (+ 1024 half 1)
+  const uint32_t Xl = S0 + XB0 + (uint32_t)kb * 4096u + (uint32_t)lane * 16u;
+
   const int32_t k0 = kt * BKG, k1 = min(Lk, k0 + BKG);
   const int32_t wk0 = k0 + kb * BKW, wk1 = min(Lk, wk0 + BKW);
   const bool wave_has_keys = wk0 < Lk;
 
-  // ---- query range of the work-group ------------------------------------
   int32_t qlo = 0, qhi = Lq;
   if (causal) qlo = span_count_lt(qs, span_pos(ks, k0));
   if (docs) {
@@ -281,164 +277,184 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
   }
   const int32_t qt0 = qlo / BQ;
   const int32_t qt1 = qhi > qlo ? (qhi + BQ - 1) / BQ : qt0;
-  const int G = a.G;
   const int nitems = (qt1 - qt0) * G;
+  const int32_t qfirst = dir < 0 ? qt1 - 1 : qt0;
 
-  // Item `it` = (query tile, head), query tiles in DESCENDING order: the
-  // work-groups resident on one XCD hold different key blocks of the same KV
-  // head, so starting them all at the last query tile has them read the same
-  // Q/dO tiles at about the same time (L2 hits instead of HBM re-reads).
-  // Q, dO tiles and the rows' LSE, Delta (and doc ids) of item `it`.  The
-  // wave that loaded the LSE (Delta) row converts it in LDS once its loads
-  // have landed (prepare): nl = -LSE log2 e, and -Delta.
-  const TileLoader<D, BQ, KNW> ldq(a.q_stride * 2, wave, lane), ldo((int64_t)a.hq * D * 2, wave, lane);
-  // The next item to issue, kept as running byte pointers (wave-uniform, in
-  // SGPRs) that move by constant steps: one head on, or back to the group's
-  // first head and one query tile down.  No division or 64-bit multiply per
-  // item.
+  // the next item to issue, as running byte pointers: heads of a query tile
+  // in turn, then the next tile in direction dir
   struct Cursor {
     int32_t qt, g;
     const char *q, *o;
     const float *l, *d;
   };
-  Cursor nx{qt1 - 1, 0,
-            (const char*)(a.q + (int64_t)(qt1 - 1) * BQ * a.q_stride + (int64_t)kvh * G * D),
-            (const char*)(a.dout + ((int64_t)(qt1 - 1) * BQ * a.hq + (int64_t)kvh * G) * D),
+  Cursor nx{qfirst, 0,
+            (const char*)(a.q + (int64_t)qfirst * BQ * a.q_stride + (int64_t)kvh * G * D),
+            (const char*)(a.dout + ((int64_t)qfirst * BQ * a.hq + (int64_t)kvh * G) * D),
             a.lse + (int64_t)kvh * G * a.lse_ld, a.delta + (int64_t)kvh * G * a.lse_ld};
-  const int64_t q_back = (int64_t)BQ * a.q_stride * 2 + (int64_t)G * D * 2;    // bytes
-  const int64_t o_back = ((int64_t)BQ * a.hq + G) * D * 2;
-  const int64_t l_back = (int64_t)G * a.lse_ld;                                // floats
-  auto advance = [&](Cursor& c) {
-    c.q += D * 2;
-    c.o += D * 2;
-    c.l += a.lse_ld;
-    c.d += a.lse_ld;
-    if (++c.g == G) {
-      c.g = 0;
-      --c.qt;
-      c.q -= q_back;
-      c.o -= o_back;
-      c.l -= l_back;
-      c.d -= l_back;
+  const int64_t q_wrap = (int64_t)dir * BQ * a.q_stride * 2 - (int64_t)G * D * 2;
+  const int64_t o_wrap = (int64_t)dir * BQ * a.hq * D * 2 - (int64_t)G * D * 2;
+  const int64_t l_back = (int64_t)G * a.lse_ld;
+  auto advance = [&](Cursor& cu) {
+    cu.q += D * 2;
+    cu.o += D * 2;
+    cu.l += a.lse_ld;
+    cu.d += a.lse_ld;
+    if (++cu.g == G) {
+      cu.g = 0;
+      cu.qt += dir;
+      cu.q += q_wrap;
+      cu.o += o_wrap;
+      cu.l -= l_back;
+      cu.d -= l_back;
     }
   };
-  auto issue = [&](const Cursor& c, uint32_t Qd, uint32_t Od, uint32_t Ld, uint32_t Dd, uint32_t Xd) {
-    if (c.qt * BQ + BQ <= Lq) {   // whole tile: precomputed lane offsets
-      ldq.load(Qd, c.q);
-      ldo.load(Od, c.o);
-    } else {                      // ragged last tile: rows clamped
-      const int head = kvh * G + c.g;
-      tile_load_lds<D, BQ, KNW>(Qd, a.q + (int64_t)head * D, a.q_stride, c.qt * BQ, Lq, wave, lane);
-      tile_load_lds<D, BQ, KNW>(Od, a.dout + (int64_t)head * D, (int64_t)a.hq * D, c.qt * BQ, Lq, wave, lane);
-    }
-    const int32_t row = min(c.qt * BQ + lane, Lq - 1);
-    if (wave == 0)
-      row_load_lds(c.l, row, Ld);
-    else if (wave == 1)
-      row_load_lds(c.d, row, Dd);
-    else if (wave == 2 && docs)
-      row_load_lds(qs.doc, row, Xd);
-  };
-  auto prepare = [&](uint32_t Ld, uint32_t Dd) {
-    if (wave == 0) lds_stf(Ld + 4 * lane, neg_lse2(lds_ldf(Ld + 4 * lane)));
-    else if (wave == 1) lds_stf(Dd + 4 * lane, -lds_ldf(Dd + 4 * lane));
-  };
-  if (nitems > 0) {
-    // the work-group's V rows (rows past Lk clamped: their keys are masked)
-    if (k0 + BKG <= Lk) {
-      const TileLoader<D, BKG, KNW> ldv(a.kv_stride * 2, wave, lane);
-      ldv.load(S0 + VT, (const char*)(a.v + (int64_t)k0 * a.kv_stride + (int64_t)kvh * D));
-      ldv.load(S0 + VT + KV_GAP<D>, (const char*)(a.k + (int64_t)k0 * a.kv_stride + (int64_t)kvh * D));
+  // item copies into tile buffer and row set tb (0..SNB-1)
+  auto issue = [&](const Cursor& cu, int tb) {
+    const uint32_t Qd = S0 + QB0 + tb * TB, Od = S0 + OB0 + tb * TB, R = S0 + RB0 + tb * 3 * RW;
+    const bool whole = cu.qt * BQ + BQ <= Lq;
+    if (whole) {
+      ldq.load(Qd, cu.q);
+      ldo.load(Od, cu.o);
     } else {
-      tile_load_lds<D, BKG, KNW>(S0 + VT, a.v + (int64_t)kvh * D, a.kv_stride, k0, Lk, wave, lane);
-      tile_load_lds<D, BKG, KNW>(S0 + VT + KV_GAP<D>, a.k + (int64_t)kvh * D, a.kv_stride, k0, Lk, wave, lane);
+      const int head = kvh * G + cu.g;
+      tile_load_lds<D, BQ, KNW>(Qd, a.q + (int64_t)head * D, a.q_stride, cu.qt * BQ, Lq, wave, lane);
+      tile_load_lds<D, BQ, KNW>(Od, a.dout + (int64_t)head * D, (int64_t)a.hq * D, cu.qt * BQ, Lq, wave, lane);
     }
-    issue(nx, S0 + Q0, S0 + O0, S0 + L0, S0 + N0, S0 + X0);
-    advance(nx);
-  }
-  const uint32_t Vw = S0 + VT + kb * (BKW * D * 2);   // this wave's 32 V rows
+    // row arrays: 16 bytes per lane for a whole tile, rows clamped otherwise
+    const int32_t row = min(cu.qt * BQ + lane, Lq - 1);
+    auto rows = [&](const void* base, uint32_t dst) {
+      if (whole) row64_load_lds(base, cu.qt * BQ, dst, lane);
+      else row_load_lds(base, row, dst);
+    };
+    if (wave == 0)
+      rows(cu.l, R);
+    else if (wave == 1)
+      rows(cu.d, R + RW);
+    else if (wave == 2 && docs)
+      rows(qs.doc, R + 2 * RW);
+  };
+  auto prepare = [&](int tb) {   // -LSE log2 e and -Delta, in place
+    const uint32_t R = S0 + RB0 + tb * 3 * RW;
+    if (wave == 0) lds_stf(R + 4 * lane, neg_lse2(lds_ldf(R + 4 * lane)));
+    else if (wave == 1) lds_stf(R + RW + 4 * lane, -lds_ldf(R + RW + 4 * lane));
+  };
 
+  // this wave's 32 K (P wave) or V (dS wave) rows as B operands (lane =
+  // key, 8 consecutive d per k step); rows past Lk clamped (their keys are
+  // masked)
   KvState<D> st;
   {
     const int32_t mykey = min(wk0 + lq, Lk - 1);
+    const bf16x8* src = (const bf16x8*)((is_ds ? a.v : a.k) + (int64_t)mykey * a.kv_stride + (int64_t)kvh * D +
+                                        hh * 8);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) { st.dka[db] = f32x16{}; st.dva[db] = f32x16{}; }
+    for (int kd = 0; kd < D / 16; ++kd) st.kv[kd] = src[kd * 2];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) st.acc[db] = f32x16{};
     st.qlim = causal ? span_count_lt(qs, span_pos(ks, mykey)) : 0;
     st.kdoc = docs ? ks.doc[mykey] : 0;
     st.kvalid = wk0 + lq < Lk;
   }
-  // wave-uniform bounds: queries >= q_all see all of the wave's keys, queries
-  // < q_none see none of them (causally)
+  // queries < q_none see none of the wave's keys, queries >= q_all every
+  // one (causally); doc ids of its first and last key
   const int32_t wlast = wave_has_keys ? wk1 - 1 : Lk - 1;
   const int32_t q_none = causal ? span_count_lt(qs, span_pos(ks, wave_has_keys ? wk0 : Lk - 1)) : 0;
   const int32_t q_all = causal ? span_count_lt(qs, span_pos(ks, wlast)) : 0;
   const int32_t kd_lo = docs ? ks.doc[wave_has_keys ? wk0 : Lk - 1] : 0;
   const int32_t kd_hi = docs ? ks.doc[wlast] : 0;
-  const float c = a.scale * LOG2E;
 
-  // lane bases with this wave's query half (rows 32 qh ..) and V rows folded
-  // in; the XOR-ed chunk and d-block steps act on bits the offsets leave clear
-  RowReader<D> rq(lane);
-  TrReader<D> tq(lane);
-  const uint32_t vb = Vw + rq.base;
-  rq.base += (uint32_t)(qh * 32 * 2 * D);
-  tq.b0 += (uint32_t)(qh * 32 * 2 * D);
-  tq.b1 += (uint32_t)(qh * 32 * 2 * D);
-
+  if (nitems > 0) {
+    issue(nx, 0);
+    advance(nx);
+  }
   wait_vm0();
-  if (nitems > 0) prepare(S0 + L0, S0 + N0);
+  if (nitems > 0) prepare(0);
   __syncthreads();
 
-  int32_t cur_qt = qt1 - 1, cur_g = 0;   // the item being computed
-  auto step = [&](int it, uint32_t Qc, uint32_t Oc, uint32_t Lc, uint32_t Dc, uint32_t Xc, uint32_t Qn,
-                  uint32_t On, uint32_t Ln, uint32_t Dn, uint32_t Xn) {
-    if (it + 1 < nitems) {
-      issue(nx, Qn, On, Ln, Dn, Xn);
-      advance(nx);
-    }
-    const int32_t qa0 = cur_qt * BQ;
-    if (++cur_g == G) { cur_g = 0; --cur_qt; }
-    const int32_t wq0 = qa0 + 32 * qh, wq1 = min(Lq, wq0 + 32);   // this wave's query rows
-    bool live = wave_has_keys && wq0 < Lq && wq1 - 1 >= q_none;
-    bool full = wq1 - wq0 == 32 && wq0 >= q_all && wk1 - wk0 == BKW;
-    if (docs) {   // both reads stay inside the 64-row buffer (qa0 < Lq)
-      const int32_t qd_lo = lds_ld4i(Xc + 4 * min(32 * qh, Lq - 1 - qa0)), qd_hi = lds_ld4i(Xc + 4 * (wq1 - 1 - qa0));
+  // item starting at row qa0 (rows of set tb): does the wave have any
+  // allowed entry in it, and is every entry of both its blocks allowed
+  auto classify = [&](int32_t qa0, int tb, bool& live, bool& full) {
+    const int32_t wq0 = qa0, wq1 = min(Lq, qa0 + BQ);
+    live = wave_has_keys && wq1 - 1 >= q_none;
+    full = wq1 - wq0 == BQ && wq0 >= q_all && wk1 - wk0 == BKW;
+    if (docs) {
+      const uint32_t Xr = S0 + RB0 + tb * 3 * RW + 2 * RW;
+      const int32_t qd_lo = lds_ld4i(Xr), qd_hi = lds_ld4i(Xr + 4 * (wq1 - 1 - qa0));
       live = live && kd_hi >= qd_lo && kd_lo <= qd_hi;
       full = full && qd_lo == qd_hi && kd_lo == kd_hi && kd_lo == qd_lo;
     }
-    live = __builtin_amdgcn_readfirstlane((int)live) != 0;   // wave-uniform: scalar branches
+    live = __builtin_amdgcn_readfirstlane((int)live) != 0;
     full = __builtin_amdgcn_readfirstlane((int)full) != 0;
-    if (live) dkdv_block<D>(st, rq, tq, Qc, Oc, vb, Lc, Dc, Xc, qa0, qh, Lq, !full, docs, c, lane);
-    wait_vm0();
-    if (it + 1 < nitems) prepare(Ln, Dn);
-    __syncthreads();
   };
-  for (int it = 0; it < nitems; it += 2) {
-    step(it, S0 + Q0, S0 + O0, S0 + L0, S0 + N0, S0 + X0, S0 + Q1, S0 + O1, S0 + L1, S0 + N1, S0 + X1);
-    if (it + 1 < nitems)
-      step(it + 1, S0 + Q1, S0 + O1, S0 + L1, S0 + N1, S0 + X1, S0 + Q0, S0 + O0, S0 + L0, S0 + N0, S0 + X0);
-  }
 
-  // ---- sum the two query halves; dK (scaled here), dV: exclusive to this
-  // work-group, read-modify-write.  The second-half wave of key block kb
-  // parks its dK^T, the first-half wave adds it and writes dK; then the
-  // roles swap for dV.  The loop ended with a barrier: the arena is free.
-  const uint32_t P = S0 + kb * (BKW * D * 4);
-  const bool writer = st.kvalid && wave_has_keys;
-  float* const krow = a.dk + ((int64_t)(wk0 + lq) * a.hkv + kvh) * D;
-  float* const vrow = a.dv + ((int64_t)(wk0 + lq) * a.hkv + kvh) * D;
-  if (qh == 1) park_acc<D>(P, st.dka, lane);
-  __syncthreads();
-  if (qh == 0) {
-    unpark_add<D>(P, st.dka, lane);
-    if (writer) add_rows<D>(krow, st.dka, a.scale, hh, a.store != 0);
-  }
-  __syncthreads();
-  if (qh == 0) park_acc<D>(P, st.dva, lane);
-  __syncthreads();
-  if (qh == 1) {
-    unpark_add<D>(P, st.dva, lane);
-    if (writer) add_rows<D>(vrow, st.dva, 1.0f, hh, a.store != 0);
+  // The two roles run separate copies of the item loop (same barriers,
+  // same copies), so that each copy's registers hold only its own carried
+  // state: P of the previous item (P wave) or its dP (dS wave).  The loop
+  // is unrolled SNB times: interval k uses buffer set k % SNB, a constant
+  // in each copy of the body.
+  auto run = [&](auto role) {
+    constexpr bool DS = decltype(role)::value;
+    bool prev_live = false;            // the previous item (its gradient runs this interval)
+    int32_t cur_qt = qfirst, cur_g = 0;
+    auto body = [&](int k, auto phase) {
+      constexpr int tb = decltype(phase)::value, tbp = (tb + SNB - 1) % SNB, tbn = (tb + 1) % SNB;
+      if (k + 1 < nitems) {
+        issue(nx, tbn);
+        advance(nx);
+      }
+      const uint32_t R = S0 + RB0 + tb * 3 * RW;
+      const uint32_t Xprev = Xl + (uint32_t)tbp * 16384u, Xcur = Xl + (uint32_t)tb * 16384u;
+      bool live = false, full = true;
+      int32_t qa0 = 0;
+      if (k < nitems) {
+        qa0 = cur_qt * BQ;
+        if (++cur_g == G) {
+          cur_g = 0;
+          cur_qt += dir;
+        }
+      }
+      if constexpr (DS) {
+        // dS wave: dS and dK of item k-1 (P from the partner), then dP of item k
+        if (prev_live) kv_grad<D, true>(st, tq, S0 + QB0 + tbp * TB, Xprev);
+        if (k < nitems) {
+          classify(qa0, tb, live, full);
+          if (live) kv_scores<D, true>(st, rq, S0 + OB0 + tb * TB, R + RW, hh);
+        }
+      } else {
+        // P wave: dV of item k-1, then S and P of item k
+        if (prev_live) kv_grad<D, false>(st, tq, S0 + OB0 + tbp * TB, 0);
+        if (k < nitems) {
+          classify(qa0, tb, live, full);
+          if (live) {
+            kv_scores<D, false>(st, rq, S0 + QB0 + tb * TB, 0, hh);
+            if (!full) {
+              kv_mask<D>(st, st.sc[0], R + 2 * RW, qa0, 0, Lq, docs, hh);
+              kv_mask<D>(st, st.sc[1], R + 2 * RW, qa0, 1, Lq, docs, hh);
+            }
+            kv_p<D>(st, R, c, hh, Xcur);
+          }
+        }
+      }
+      prev_live = live;
+      wait_vm0();
+      if (k + 1 < nitems) prepare(tbn);
+      __syncthreads();
+    };
+    for (int k = 0; k <= nitems; k += SNB) {
+      static_assert(SNB == 3, "the unrolled body below assumes three buffer sets");
+      body(k, std::integral_constant<int, 0>{});
+      if (k + 1 > nitems) break;
+      body(k + 1, std::integral_constant<int, 1>{});
+      if (k + 2 > nitems) break;
+      body(k + 2, std::integral_constant<int, 2>{});
+    }
+  };
+  if (is_ds) run(std::integral_constant<bool, true>{});
+  else run(std::integral_constant<bool, false>{});
+
+  if (st.kvalid && wave_has_keys) {
+    float* const dst = (is_ds ? a.dk : a.dv) + ((int64_t)(wk0 + lq) * a.hkv + kvh) * D;
+    add_rows<D>(dst, st.acc, is_ds ? a.scale : 1.0f, hh, a.store != 0);
   }
 }
 
@@ -679,7 +695,7 @@ hipError_t launch_bwd_bf16_dkdv(const BwdParams& p, hipStream_t stream) {
   BwdParams a = p;
   a.nkt = (span_len(a.ks) + BKG - 1) / BKG;
   a.n_work = a.nkt * a.hkv;
-  const int32_t grid = xcd_grid(a.hkv, a.nkt);
+  const int32_t grid = dkdv_grid(a.hkv, a.nkt);
   if (a.d == 128) hipLaunchKernelGGL(dkdv_bf16_kernel<128>, dim3(grid), dim3(64 * KNW), 0, stream, a);
   else hipLaunchKernelGGL(dkdv_bf16_kernel<64>, dim3(grid), dim3(64 * KNW), 0, stream, a);
   return hipGetLastError();

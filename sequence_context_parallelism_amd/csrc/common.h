@@ -150,4 +150,62 @@ __host__ inline int32_t xcd_grid(int32_t ngroups, int32_t nidx) {
 
 __host__ inline int32_t round_up8(int32_t n) { return (n + 7) & ~7; }
 
+// Work order of a KV-outer kernel whose items are the `nkt` key tiles of
+// `ngroups` KV heads, each running over the query tiles that see it (causal:
+// key tile kt sees nkt - kt of them, in units of its width).  Key tiles kt
+// and nkt-1-kt are partners: one XCD runs the first members of DKDV_COHORT
+// pairs at once, walking their query tiles last to first (dir = -1), and
+// then the second members in the reverse order of the first members'
+// finishing, walking first to last (dir = +1).  On a causal share a pair's
+// two parts together take the same time for every pair, and at any moment
+// the cohort's work-groups stand on one of two query tiles, so the tiles
+// they copy are shared through the XCD's L2.  Group placement follows
+// xcd_work.  Returns false for a padding block.
+constexpr int32_t DKDV_COHORT = 32;   // work-groups one XCD holds at once (one per CU)
+
+__host__ __device__ inline int32_t dkdv_pair_slots(int32_t npairs) {
+  return 2 * DKDV_COHORT * ((npairs + DKDV_COHORT - 1) / DKDV_COHORT);
+}
+
+__host__ __device__ inline bool dkdv_work(int32_t b, int32_t ngroups, int32_t nkt, int32_t& group, int32_t& kt, int32_t& dir) {
+  const int32_t xcd = b & 7, slot = b >> 3;
+  const int32_t np = (nkt + 1) / 2;
+  int32_t first, stride, lslot;   // this XCD's pairs of `group`: first, first + stride, ...
+  if ((8 % ngroups) == 0) {
+    const int32_t per = 8 / ngroups;
+    group = xcd % ngroups;
+    first = xcd / ngroups;
+    stride = per;
+    lslot = slot;
+  } else if ((ngroups % 8) == 0) {
+    const int32_t spg = dkdv_pair_slots(np);
+    group = xcd + 8 * (slot / spg);
+    first = 0;
+    stride = 1;
+    lslot = slot % spg;
+  } else {   // no pairing: key tiles in order, groups interleaved
+    group = b % ngroups;
+    kt = b / ngroups;
+    dir = -1;
+    return kt < nkt;
+  }
+  const int32_t round = lslot / DKDV_COHORT, u = lslot % DKDV_COHORT;
+  const bool second = (round & 1) != 0;
+  const int32_t i = (round >> 1) * DKDV_COHORT + (second ? DKDV_COHORT - 1 - u : u);
+  const int32_t p = first + stride * i;
+  if (p >= np) return false;
+  kt = second ? nkt - 1 - p : p;
+  dir = second ? 1 : -1;
+  return !(second && kt == p);   // an odd count's middle tile has no partner
+}
+
+__host__ inline int32_t dkdv_grid(int32_t ngroups, int32_t nkt) {
+  const int32_t np = (nkt + 1) / 2;
+  int64_t n;
+  if ((8 % ngroups) == 0) n = 8 * (int64_t)dkdv_pair_slots((np + 8 / ngroups - 1) / (8 / ngroups));
+  else if ((ngroups % 8) == 0) n = (int64_t)ngroups * dkdv_pair_slots(np);
+  else n = (((int64_t)ngroups * nkt + 7) / 8) * 8;
+  return (int32_t)n;
+}
+
 }  // namespace cp

@@ -82,6 +82,16 @@ __device__ inline void row_load_lds(const void* base, int32_t idx, uint32_t lds)
                "{m0}"(lds) : "memory");
 }
 
+// 64 consecutive 4-byte elements (256 bytes) at base + 4 idx0 into LDS
+// [lds, +256): lanes 0..15 load 16 bytes each, the rest of the wave is masked
+// off.  One instruction like row_load_lds, but a quarter of the lane-elements
+// for the LDS DMA to write.  All 64 elements must be in bounds.
+__device__ inline void row64_load_lds(const void* base, int32_t idx0, uint32_t lds, int lane) {
+  if (lane < 16)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"((uint32_t)idx0 * 4u + (uint32_t)lane * 16u),
+                 "s"(buf_rsrc(base)), "{m0}"(lds) : "memory");
+}
+
 // Issue the direct-to-LDS loads of an R x D tile at LDS address `dst` whose
 // row i sits at src + i * stride (rows past `valid_rows` are clamped to
 // valid_rows - 1, so every load is in bounds; callers mask those rows).  NW
