@@ -114,7 +114,7 @@ struct KvState {
 // chains interleaved: S (P wave: A = Q rows) or dP (dS wave: A = dO rows,
 // accumulators from -Delta at NDt).
 template <int D, bool DS>
-__device__ inline void kv_scores(KvState<D>& st, const RowReader<D>& rq, uint32_t Tt, uint32_t NDt, int hh) {
+__device__ inline void kv_scores(KvState<D>& st, const RowLanes<D>& rq, uint32_t Tt, uint32_t NDt, int hh) {
   constexpr int NKD = D / 16;
   if constexpr (DS) {
 #pragma unroll
@@ -183,7 +183,7 @@ __device__ inline void kv_p(KvState<D>& st, uint32_t Nl, float c, int hh, uint32
 // (P wave, g = st.pb) or dK^T += Q^T dS (dS wave, dS formed here from the
 // partner's P at Xp and st.sc; block 1's dS is formed between block 0's MFMAs).
 template <int D, bool DS>
-__device__ inline void kv_grad(KvState<D>& st, const TrReader<D>& tq, uint32_t At, uint32_t Xp) {
+__device__ inline void kv_grad(KvState<D>& st, const TrLanes<D>& tq, uint32_t At, uint32_t Xp) {
   constexpr int NDB = D / 32, NM = 2 * NDB, PER = 16 / NM;
   bf16x8 g0[2], g1[2], p1[2];
   if constexpr (DS) {
@@ -260,8 +260,11 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
   const int G = a.G;
   const TileLoader<D, BQ, KNW> ldq(a.q_stride * 2, wave, lane), ldo((int64_t)a.hq * D * 2, wave, lane);
   const float c = a.scale * LOG2E;
-  const RowReader<D> rq(lane);
-  const TrReader<D> tq(lane);
+  // lane parts of the row and transposed reads, for the Q tiles (from the arena
+  // start) and the dO tiles (from their region's start): each role reads one
+  // kind of tile row-wise and the other transposed
+  const RowLanes<D> rq(RowReader<D>(lane), S0 + QB0), rqo(RowReader<D>(lane), S0 + OB0);
+  const TrLanes<D> tq(TrReader<D>(lane), S0 + QB0), tqo(TrReader<D>(lane), S0 + OB0);
   // this lane's 16-byte slot in the exchange area of pair kb: + buf * 16384 + qb * 2048 (+ 1024 half 1)
   const uint32_t Xl = S0 + XB0 + (uint32_t)kb * 4096u + (uint32_t)lane * 16u;
 
@@ -415,18 +418,18 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
       }
       if constexpr (DS) {
         // dS wave: dS and dK of item k-1 (P from the partner), then dP of item k
-        if (prev_live) kv_grad<D, true>(st, tq, S0 + QB0 + tbp * TB, Xprev);
+        if (prev_live) kv_grad<D, true>(st, tq, tbp * TB, Xprev);
         if (k < nitems) {
           classify(qa0, tb, live, full);
-          if (live) kv_scores<D, true>(st, rq, S0 + OB0 + tb * TB, R + RW, hh);
+          if (live) kv_scores<D, true>(st, rqo, tb * TB, R + RW, hh);
         }
       } else {
         // P wave: dV of item k-1, then S and P of item k
-        if (prev_live) kv_grad<D, false>(st, tq, S0 + OB0 + tbp * TB, 0);
+        if (prev_live) kv_grad<D, false>(st, tqo, tbp * TB, 0);
         if (k < nitems) {
           classify(qa0, tb, live, full);
           if (live) {
-            kv_scores<D, false>(st, rq, S0 + QB0 + tb * TB, 0, hh);
+            kv_scores<D, false>(st, rq, tb * TB, 0, hh);
             if (!full) {
               kv_mask<D>(st, st.sc[0], R + 2 * RW, qa0, 0, Lq, docs, hh);
               kv_mask<D>(st, st.sc[1], R + 2 * RW, qa0, 1, Lq, docs, hh);

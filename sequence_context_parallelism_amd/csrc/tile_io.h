@@ -240,6 +240,45 @@ struct TrReader {
   }
 };
 
+// The same reads with every lane part precomputed once (one register per d
+// step or d block) and kept opaque to the compiler, which would otherwise
+// recompute the XORs in every tile of a loop whose registers are tight.
+// `off` is added to every lane part (a tile region's start, so that the
+// offsets left to the instruction stay below its 64 KiB field).
+template <int D>
+struct RowLanes {
+  uint32_t a[D / 16];
+  __device__ RowLanes(const RowReader<D>& r, uint32_t off) {
+#pragma unroll
+    for (int kd = 0; kd < D / 16; ++kd) {
+      a[kd] = (r.base ^ (uint32_t)(kd << 5)) + off;
+      asm volatile("" : "+v"(a[kd]));
+    }
+  }
+  __device__ inline bf16x8 at(uint32_t tile, int rb, int kd) const {
+    return lds_ld16(tile + (uint32_t)(rb * 32 * 2 * D) + a[kd]);
+  }
+};
+
+template <int D>
+struct TrLanes {
+  uint32_t a0[D / 32], a1[D / 32];
+  __device__ TrLanes(const TrReader<D>& r, uint32_t off) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      a0[db] = (r.b0 ^ (uint32_t)(db << 6)) + off;
+      a1[db] = (r.b1 ^ (uint32_t)(db << 6)) + off;
+      asm volatile("" : "+v"(a0[db]), "+v"(a1[db]));
+    }
+  }
+  __device__ inline bf16x8 at(uint32_t tile, int R, int db) const {
+    const uint32_t t = tile + (uint32_t)(R * 2 * D);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)(t + a0[db]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)(t + a1[db]));
+    return cat8(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
+  }
+};
+
 // Pin values in place: an empty asm that reads them, so the compiler cannot
 // sink their computation into a later block (which would undo an
 // interleaving above it).
