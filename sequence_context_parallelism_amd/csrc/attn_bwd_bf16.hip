@@ -250,8 +250,12 @@ __global__ __launch_bounds__(64 * KNW, 1) void dkdv_bf16_kernel(BwdParams a) {
   const int lq = lane & 31, hh = lane >> 5;
 
   // one key tile of one KV head; dir: the order of its query tiles
-  int32_t kvh, kt, dir;
-  if (!dkdv_work(blockIdx.x, a.hkv, a.nkt, kvh, kt, dir)) return;
+  int32_t kvh, kt, dir = -1;
+  if (a.pair) {
+    if (!dkdv_work(blockIdx.x, a.hkv, a.nkt, kvh, kt, dir)) return;
+  } else if (!xcd_work(blockIdx.x, a.hkv, a.nkt, kvh, kt)) {
+    return;
+  }
 
   const SpanD qs = a.qs, ks = a.ks;
   const int32_t Lq = span_len(qs), Lk = span_len(ks);
@@ -698,7 +702,15 @@ hipError_t launch_bwd_bf16_dkdv(const BwdParams& p, hipStream_t stream) {
   BwdParams a = p;
   a.nkt = (span_len(a.ks) + BKG - 1) / BKG;
   a.n_work = a.nkt * a.hkv;
-  const int32_t grid = dkdv_grid(a.hkv, a.nkt);
+  // Partner key tiles pay off when a key tile's work falls linearly with its
+  // index: a causal pair of spans whose key positions reach into the query
+  // positions.  With document masks, or with every key before every query
+  // (all key tiles equally heavy), the heavy-first order shares the copied
+  // tiles as well and measured faster.
+  const SpanD& qs = a.qs;
+  const SpanD& ks = a.ks;
+  a.pair = a.causal && qs.doc == nullptr && span_pos(ks, span_len(ks) - 1) >= span_pos(qs, 0);
+  const int32_t grid = a.pair ? dkdv_grid(a.hkv, a.nkt) : xcd_grid(a.hkv, a.nkt);
   if (a.d == 128) hipLaunchKernelGGL(dkdv_bf16_kernel<128>, dim3(grid), dim3(64 * KNW), 0, stream, a);
   else hipLaunchKernelGGL(dkdv_bf16_kernel<64>, dim3(grid), dim3(64 * KNW), 0, stream, a);
   return hipGetLastError();

@@ -53,6 +53,7 @@ struct BwdParams {
   int store;                 // bf16 path: 1 = write the gradients (the call's pairs are all of them), 0 = add
   // filled in by the launcher
   int nkt, n_work;
+  int pair;                  // dK/dV work order: partner key tiles (dkdv_work) or heavy-first (xcd_work)
   int heads_per_wg, qblocks_per_wg, nqt;
 };
 
