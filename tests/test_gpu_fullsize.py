@@ -5,6 +5,8 @@ workspace), on outputs the fp64 oracle computes exactly:
 * O, LSE and dQ of sampled (row, head) pairs -- each row exact over all of
   its keys (512 rows for the 64K Ulysses share, 256 for the 1M USP share, 64
   for the 128K ring and packed-document workloads);
+* the same for rank P-1 of the 128K ring, whose rows sit in the middle of
+  the sequence (test_full_size_ring_last_rank);
 * dK and dV of sampled keys spread over the sequence -- key 0, keys of the
   first 128-key block, of middle blocks and of the last one.  The oracle
   first runs its forward over every query row that attends those keys (one
@@ -249,3 +251,91 @@ def test_full_size_dkdv_long_paths(gpu_lib, workloads, name):
     _say(f"[fullsize] {name}: keys at positions {np.asarray(kpos)[keys].tolist()}: dK {e_dk:.2e} dV {e_dv:.2e}")
     assert e_dk <= grad_tol(dk_ref, tol["grad"])
     assert e_dv <= grad_tol(dv_ref, tol["grad"])
+
+
+def test_full_size_ring_last_rank(gpu_lib):
+    """Rank P-1 of the 128K zigzag ring (its chunks P-1 and P, the middle of the
+    sequence, so its steps mix diagonal, full and skipped blocks differently
+    from rank 0): sampled rows' O, LSE, dQ and sampled keys' dK/dV (this
+    rank's rows' contributions) against the oracle, through cp_ring_emulate
+    at the bench's shapes."""
+    torch.cuda.empty_cache()
+    S, hq, hkv, d, P = 131072, 32, 8, 128, 8
+    r = P - 1
+    n = S // P
+    seed = cpinputs.SEEDS["ring_128k"] + 17
+    q, k, v = cpinputs.normal_torch(seed, [(S, hq, d), (S, hkv, d), (S, hkv, d)], "cuda", torch.bfloat16)
+    (dout,) = cpinputs.normal_torch(seed + 1, [(n, hq, d)], "cuda", torch.bfloat16)
+    sh = cp.make_shape(hq, hkv, d, hq * d, hkv * d, 1.0 / math.sqrt(d), True, cp.CP_BF16)
+    o = torch.empty(n, hq, d, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(hq, n, device="cuda")
+    dq = torch.empty(n, hq, d, device="cuda")
+    dk = torch.empty(S, hkv, d, device="cuda")
+    dv = torch.empty_like(dk)
+    ws = cp.workspace(cp.cp_ring_workspace_bytes(sh, S, P, r, cp.CP_BF16, True))
+    _say(f"[fullsize] ring_128k rank {r}: running the ring")
+    cp.cp_ring_emulate(sh, S, P, r, q, k, v, None, o, lse, dout, dq, dk, dv, workspace=ws)
+    torch.cuda.synchronize()
+
+    qpos = Z.rank_positions(S, P, r)
+    kpos = np.concatenate([Z.rank_positions(S, P, j) for j in range(P)])
+    scale = 1.0 / math.sqrt(d)
+    tol = TOL[torch.bfloat16]
+    qr = q[r * n:(r + 1) * n]                      # this rank's rows (sharded order)
+    kh = k.float().cpu().numpy()
+    vh = v.float().cpu().numpy()
+
+    # sampled rows: O, LSE, dQ
+    rng = np.random.default_rng(4242)
+    rows = np.unique(np.concatenate([[0, n // 2 - 1, n // 2, n - 1], rng.choice(n, size=60, replace=False)]))
+    q_s, do_s = _rows(qr, rows), _rows(dout, rows)
+    _say(f"[fullsize] ring_128k rank {r}: oracle on {len(rows)} rows x {hq} heads")
+
+    def one(idx):
+        sub = rows[idx]
+        sel = _key_range(kpos, None, qpos[sub], None)
+        kp = np.asarray(kpos)[sel]
+        o_r, l_r = A.forward(q_s[idx], kh[sel], vh[sel], qpos[sub], kp, scale=scale, causal=True)
+        dq_r, _, _ = A.backward(q_s[idx], kh[sel], vh[sel], do_s[idx], l_r, A.delta(o_r, do_s[idx]), qpos[sub],
+                                kp, scale=scale, causal=True)
+        return idx, o_r, l_r, dq_r
+
+    parts = np.array_split(np.arange(len(rows)), min(len(rows), 4 * WORKERS))
+    o_ref = np.zeros((len(rows), hq, d))
+    lse_ref = np.zeros((hq, len(rows)))
+    dq_ref = np.zeros_like(o_ref)
+    with _blas_single_thread(), cf.ThreadPoolExecutor(WORKERS) as ex:
+        for idx, o_r, l_r, dq_r in ex.map(one, parts):
+            o_ref[idx], lse_ref[:, idx], dq_ref[idx] = o_r, l_r, dq_r
+    e_o = max_abs(_rows(o, rows), o_ref)
+    e_l = lse_err(lse[:, torch.as_tensor(rows, device=lse.device)].double().cpu().numpy(), lse_ref)
+    e_dq = max_abs(_rows(dq, rows), dq_ref)
+    _say(f"[fullsize] ring_128k rank {r}: O {e_o:.2e} LSE {e_l:.2e} dQ {e_dq:.2e}")
+    assert e_o <= tol["o"]
+    assert e_l <= tol["lse"]
+    assert e_dq <= grad_tol(dq_ref, tol["grad"])
+
+    # sampled keys: dK/dV of this rank's rows, KV head 0 and its query heads
+    keys = []
+    for j in range(P):
+        keys += [j * n, j * n + 1, j * n + int(rng.integers(2, 128)), j * n + n // 2 + 7]
+    keys = np.array(keys)
+    g, grp = 0, hq // hkv
+    kmin = int(np.min(np.asarray(kpos)[keys]))
+    att = np.nonzero(qpos >= kmin)[0]
+    q_a = qr[torch.as_tensor(att, device=q.device)][:, g * grp:(g + 1) * grp].double().cpu().numpy()
+    do_a = dout[torch.as_tensor(att, device=q.device)][:, g * grp:(g + 1) * grp].double().cpu().numpy()
+    k1 = k[:, g:g + 1].double().cpu().numpy()
+    v1 = v[:, g:g + 1].double().cpu().numpy()
+    _say(f"[fullsize] ring_128k rank {r}: dK/dV of {len(keys)} keys, oracle forward over {len(att)} rows x {grp} heads")
+    o_a, lse_a = _parallel_forward(q_a, k1, v1, qpos[att], kpos, None, None, scale, 1024)
+    dlt_a = A.delta(o_a, do_a)
+    dk_ref, dv_ref = A.dkv_keys(q_a, k1, v1, do_a, lse_a, dlt_a, qpos[att], kpos, keys, np.zeros(len(keys), int),
+                                scale=scale, causal=True)
+    e_dk = max_abs(_rows(dk, keys)[:, g], dk_ref)
+    e_dv = max_abs(_rows(dv, keys)[:, g], dv_ref)
+    _say(f"[fullsize] ring_128k rank {r}: dK {e_dk:.2e} dV {e_dv:.2e}")
+    assert e_dk <= grad_tol(dk_ref, tol["grad"])
+    assert e_dv <= grad_tol(dv_ref, tol["grad"])
+    del q, k, v, dout, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
