@@ -27,6 +27,8 @@ CASES = [
     ("one_row_half_one_key_block", 4, 1, 128, (0, 33), (0, 129), False, False),   # 2nd query half: 1 row
     ("all_rows_empty", 4, 2, 128, (0, 40), (100, 64), True, False),   # every key after every query
     ("no_keys", 4, 2, 64, (0, 70), (0, 0), True, False),              # empty key span
+    ("causal_g1_nine_key_tiles", 2, 2, 128, (0, 1100), (0, 1100), True, False),   # partner key tiles, odd count
+    ("causal_eight_kv_heads", 16, 8, 64, (0, 900), (0, 900), True, False),        # one KV head per XCD
 ]
 
 
